@@ -1,0 +1,316 @@
+"""Pins of the CPU oracle against things other than itself: textbook
+routines, closed forms, invariants, brute force on tiny inputs and a
+hand-derived worked example.  CPU only."""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import bruteforce as bf
+from moe_inputs import f32_to_bf16_bits, bf16_bits_to_f32
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(s):
+    return np.random.default_rng(s)
+
+
+def _np_gelu(a):
+    return 0.5 * a * (1.0 + np.vectorize(math.erf)(a / math.sqrt(2.0)))
+
+
+def _as_f64(a):
+    return bf16_bits_to_f32(a).astype(np.float64) if a.dtype == np.uint16 else a.astype(np.float64)
+
+
+# ---------------------------------------------------------------- gate -----
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_gate_matches_numpy_matmul(orc, dtype):
+    r = _rng(1)
+    T, d, E = 37, 24, 11
+    x = r.standard_normal((T, d)).astype(np.float32)
+    if dtype == "bf16":
+        x = f32_to_bf16_bits(x)
+    Wg = r.standard_normal((d, E)).astype(np.float32)
+    bg = r.standard_normal(E).astype(np.float32)
+    ref = _as_f64(x) @ Wg.astype(np.float64) + bg.astype(np.float64)
+    got = orc.gate(x, Wg, bg)
+    np.testing.assert_allclose(got, ref, rtol=1e-13, atol=1e-13)
+    ref0 = _as_f64(x) @ Wg.astype(np.float64)
+    np.testing.assert_allclose(orc.gate(x, Wg, None), ref0, rtol=1e-13, atol=1e-13)
+
+
+def test_gate_exact_on_integers(orc):
+    r = _rng(2)
+    x = r.integers(-3, 4, (9, 5)).astype(np.float32)
+    Wg = r.integers(-3, 4, (5, 7)).astype(np.float32)
+    assert np.array_equal(orc.gate(x, Wg), x.astype(np.int64) @ Wg.astype(np.int64))
+
+
+# --------------------------------------------------------------- route -----
+@pytest.mark.parametrize("seed,E,k", [(0, 8, 2), (1, 5, 1), (2, 6, 6), (3, 8, 8), (4, 16, 3)])
+def test_route_selection_bruteforce(orc, seed, E, k):
+    r = _rng(seed)
+    T = 40
+    # few distinct values so that ties are frequent, plus -0.0/+0.0 pairs
+    L = r.integers(-2, 3, (T, E)).astype(np.float32)
+    L[r.random((T, E)) < 0.2] = -0.0
+    L[:5] = r.standard_normal((5, E)).astype(np.float32)
+    idx, w = orc.route(L, k)
+    for t in range(T):
+        assert list(idx[t]) == bf.select([float(v) for v in L[t]], k)
+
+
+def test_route_all_tied_picks_lowest(orc):
+    L = np.full((3, 10), 0.25, np.float32)
+    L[1] = -0.0
+    L[2, ::2] = 0.0
+    L[2, 1::2] = -0.0
+    idx, w = orc.route(L, 4)
+    assert (idx == np.arange(4)).all()
+    np.testing.assert_allclose(w, 0.25, rtol=0, atol=1e-15)
+
+
+def test_route_weight_closed_forms(orc):
+    # k = 1 -> weight exactly 1
+    L = _rng(5).standard_normal((7, 9)).astype(np.float32)
+    _, w1 = orc.route(L, 1)
+    assert (w1 == 1.0).all()
+    # a logit gap of tau*ln 3 gives weights (3/4, 1/4), for two temperatures
+    for tau in (1.0, 0.2):
+        gap = np.float32(tau * math.log(3.0))
+        L2 = np.array([[0.5, 0.5 - gap, -9.0]], np.float32)
+        g = float(np.float32(0.5)) - float(np.float32(np.float32(0.5) - gap))
+        idx, w = orc.route(L2, 2, tau)
+        assert list(idx[0]) == [0, 1]
+        expect = 1.0 / (1.0 + math.exp(-g / tau))
+        assert abs(w[0, 0] - expect) < 1e-15 and abs(w[0, 0] - 0.75) < 1e-6
+        assert abs(w[0, 1] - (1 - expect)) < 1e-15
+
+
+def test_route_invariants(orc):
+    L = _rng(6).standard_normal((200, 64)).astype(np.float32)
+    for k, tau in ((2, 1.0), (8, 0.2)):
+        idx, w = orc.route(L, k, tau)
+        assert all(len(set(row)) == k for row in idx.tolist())
+        np.testing.assert_allclose(w.sum(1), 1.0, rtol=0, atol=1e-15)
+        assert (np.diff(w, axis=1) <= 0).all()
+        sel = np.take_along_axis(L, idx, 1)
+        assert (np.diff(sel, axis=1) <= 0).all()
+        # every unselected logit is <= the smallest selected one
+        mask = np.ones_like(L, bool)
+        np.put_along_axis(mask, idx, False, 1)
+        assert (np.where(mask, L, -np.inf).max(1) <= sel[:, -1]).all()
+
+
+# ------------------------------------------------------------ capacity -----
+@pytest.mark.parametrize("T,E,k,cf,cap", [
+    (4096, 16, 2, 1.25, 640), (8192, 64, 2, 2.0, 512), (32768, 256, 2, 1.25, 320),
+    (8192, 128, 8, 0.0, 8192), (256, 8, 2, 0.0, 256), (256, 8, 2, -1.0, 256),
+    (200, 8, 2, 0.02, 1), (10, 1, 1, 5.0, 10), (100, 3, 1, 0.75, 25), (100, 3, 1, 0.5, 17),
+    (5, 3, 2, 0.5, 2), (1000, 12, 3, 1.0, 250)])
+def test_capacity_closed_forms(orc, T, E, k, cf, cap):
+    assert orc.capacity(T, E, k, cf) == cap
+
+
+# ------------------------------------------------------------ dispatch -----
+@pytest.mark.parametrize("seed,T,E,k,cap", [(0, 30, 4, 2, 9), (1, 25, 5, 3, 4), (2, 40, 3, 1, 40),
+                                            (3, 17, 6, 2, 1), (4, 1, 4, 2, 1), (5, 33, 8, 8, 20)])
+def test_dispatch_bruteforce_and_invariants(orc, seed, T, E, k, cap):
+    r = _rng(seed)
+    L = r.standard_normal((T, E)).astype(np.float32)
+    L[:, 0] += 1.0  # skew toward expert 0 so that drops happen
+    idx, _ = orc.route(L, k)
+    got = orc.dispatch(idx, E, cap)
+    ref = bf.dispatch(idx.tolist(), E, cap)
+    for key in ("routed", "counts", "offsets", "perm", "slot"):
+        assert np.array_equal(np.asarray(got[key]), np.asarray(ref[key])), key
+    counts, offsets, perm, slot = got["counts"], got["offsets"], got["perm"], got["slot"]
+    S = int(offsets[-1])
+    drops = int((slot < 0).sum())
+    assert counts.sum() == T * k - drops and (counts <= cap).all()
+    assert (got["routed"] >= counts).all() and got["routed"].sum() == T * k
+    # bijection between kept slots and rows [0, S)
+    rows = np.sort(slot[slot >= 0])
+    assert np.array_equal(rows, np.arange(S))
+    for t in range(T):
+        for j in range(k):
+            if slot[t, j] >= 0:
+                assert perm[slot[t, j]] == t
+                e = idx[t, j]
+                assert offsets[e] <= slot[t, j] < offsets[e + 1]
+            else:
+                e = idx[t, j]
+                seg = perm[offsets[e]:offsets[e + 1]]
+                assert len(seg) == cap and (seg < t).all()
+    for e in range(E):
+        seg = perm[offsets[e]:offsets[e + 1]]
+        assert (np.diff(seg) > 0).all()
+    assert (perm[S:] == -1).all()
+
+
+def test_dispatch_two_expert_closed_form(orc):
+    T, c = 50, 13
+    L = np.full((T, 6), -1.0, np.float32)
+    L[:, 0] = 2.0
+    L[:, 1] = 1.0
+    idx, _ = orc.route(L, 2)
+    got = orc.dispatch(idx, 6, c)
+    assert int((got["slot"] < 0).sum()) == 2 * (T - c)
+    assert np.array_equal(got["perm"][:c], np.arange(c))
+    assert np.array_equal(got["perm"][c:2 * c], np.arange(c))
+    assert (got["slot"][:c] >= 0).all() and (got["slot"][c:] < 0).all()
+
+
+def test_dispatch_worked_example(orc):
+    g = json.load(open(os.path.join(GOLDEN, "dispatch_worked_example.json")))
+    L = np.array(g["logits"], np.float32)
+    L[4, 0] = -0.0
+    assert orc.capacity(g["T"], g["E"], g["k"], g["capacity_factor"]) == g["cap"]
+    idx, w = orc.route(L, g["k"], g["temperature"])
+    assert idx.tolist() == g["idx"]
+    np.testing.assert_allclose(w, np.array(g["w"]), rtol=0, atol=1e-15)
+    got = orc.dispatch(idx, g["E"], g["cap"])
+    for key in ("routed", "counts", "offsets", "perm", "slot"):
+        assert np.asarray(got[key]).tolist() == g[key], key
+    assert abs(orc.aux(got["counts"], g["T"], g["k"], g["aux_lambda"]) - g["aux"]) < 1e-18
+
+
+# ---------------------------------------------------------------- GELU -----
+def test_gelu_textbook_values(orc):
+    # Phi(1) and Phi(-1) of the standard normal distribution
+    assert abs(orc.gelu(1.0) - 0.8413447460685429) < 1e-15
+    assert abs(orc.gelu(-1.0) + 0.15865525393145707) < 1e-15
+    assert orc.gelu(0.0) == 0.0
+    # Phi(2) = 0.9772498680518208
+    assert abs(orc.gelu(2.0) - 2 * 0.9772498680518208) < 1e-15
+    for u in (0.3, 1.7, 4.2, 11.0):
+        assert abs((orc.gelu(u) - orc.gelu(-u)) - u) <= 4e-16 * max(1.0, u)
+    assert abs(orc.gelu(40.0) - 40.0) < 1e-12 and abs(orc.gelu(-40.0)) < 1e-12
+
+
+# ----------------------------------------------------------------- FFN -----
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_one_expert_dense_ffn_matches_numpy(orc, dtype):
+    r = _rng(7)
+    T, d, dff = 23, 12, 20
+    x = r.standard_normal((T, d)).astype(np.float32)
+    W1 = (r.standard_normal((1, d, dff)) / math.sqrt(d)).astype(np.float32)
+    W2 = (r.standard_normal((1, dff, d)) / math.sqrt(dff)).astype(np.float32)
+    b1 = r.standard_normal((1, dff)).astype(np.float32)
+    b2 = r.standard_normal((1, d)).astype(np.float32)
+    Wg = r.standard_normal((d, 1)).astype(np.float32)
+    if dtype == "bf16":
+        x, W1, W2 = f32_to_bf16_bits(x), f32_to_bf16_bits(W1), f32_to_bf16_bits(W2)
+    out = orc.layer_forward(x, Wg, None, W1, b1, W2, b2, k=1, cf=0.0)
+    ref = _np_gelu(_as_f64(x) @ _as_f64(W1)[0] + b1[0]) @ _as_f64(W2)[0] + b2[0]
+    np.testing.assert_allclose(out["y"], ref, rtol=1e-12, atol=1e-12)
+    assert (out["w"] == 1.0).all() and out["counts"].tolist() == [T]
+
+
+def _identity_experts(E, d, dff, dtype):
+    assert dff >= 2 * d
+    W1 = np.zeros((E, d, dff), np.float32)
+    W2 = np.zeros((E, dff, d), np.float32)
+    I = np.eye(d, dtype=np.float32)
+    W1[:, :, :d] = I
+    W1[:, :, d:2 * d] = -I
+    W2[:, :d, :] = I
+    W2[:, d:2 * d, :] = -I
+    if dtype == "bf16":
+        W1, W2 = f32_to_bf16_bits(W1), f32_to_bf16_bits(W2)
+    return W1, np.zeros((E, dff), np.float32), W2, np.zeros((E, d), np.float32)
+
+
+@pytest.mark.parametrize("dtype,cf", [("fp32", 0.0), ("bf16", 0.0), ("bf16", 0.6)])
+def test_identity_experts_reproduce_x(orc, dtype, cf):
+    r = _rng(8)
+    T, d, dff, E, k = 60, 8, 24, 5, 2
+    x = r.standard_normal((T, d)).astype(np.float32)
+    if dtype == "bf16":
+        x = f32_to_bf16_bits(x)
+    Wg = r.standard_normal((d, E)).astype(np.float32)
+    W1, b1, W2, b2 = _identity_experts(E, d, dff, dtype)
+    out = orc.layer_forward(x, Wg, None, W1, b1, W2, b2, k=k, cf=cf)
+    kept_w = np.where(out["slot"] >= 0, out["w"], 0.0).sum(1)
+    np.testing.assert_allclose(out["y"], kept_w[:, None] * _as_f64(x), rtol=1e-14, atol=1e-14)
+    if cf == 0.0:
+        np.testing.assert_allclose(out["y"], _as_f64(x), rtol=1e-14, atol=1e-14)
+    else:
+        assert (out["slot"] < 0).any()
+
+
+def test_k_equals_e_is_dense_soft_moe(orc):
+    r = _rng(9)
+    T, d, dff, E, tau = 31, 10, 14, 4, 0.5
+    x = r.standard_normal((T, d)).astype(np.float32)
+    Wg = r.standard_normal((d, E)).astype(np.float32)
+    W1 = r.standard_normal((E, d, dff)).astype(np.float32) / 3
+    W2 = r.standard_normal((E, dff, d)).astype(np.float32) / 3
+    b1 = r.standard_normal((E, dff)).astype(np.float32)
+    b2 = r.standard_normal((E, d)).astype(np.float32)
+    out = orc.layer_forward(x, Wg, None, W1, b1, W2, b2, k=E, cf=0.0, tau=tau)
+    L = out["logits32"].astype(np.float64) / tau
+    g = np.exp(L - L.max(1, keepdims=True))
+    g /= g.sum(1, keepdims=True)
+    ref = np.zeros((T, d))
+    for e in range(E):
+        fe = _np_gelu(x.astype(np.float64) @ W1[e] + b1[e]) @ W2[e].astype(np.float64) + b2[e]
+        ref += g[:, e:e + 1] * fe
+    np.testing.assert_allclose(out["y"], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_token_permutation_equivariance(orc):
+    r = _rng(10)
+    T, d, dff, E, k = 50, 16, 32, 6, 2
+    x = f32_to_bf16_bits(r.standard_normal((T, d)).astype(np.float32))
+    Wg = r.standard_normal((d, E)).astype(np.float32)
+    W1 = f32_to_bf16_bits(r.standard_normal((E, d, dff)).astype(np.float32) / 4)
+    W2 = f32_to_bf16_bits(r.standard_normal((E, dff, d)).astype(np.float32) / 4)
+    b1 = r.standard_normal((E, dff)).astype(np.float32)
+    b2 = r.standard_normal((E, d)).astype(np.float32)
+    p = r.permutation(T)
+    a = orc.layer_forward(x, Wg, None, W1, b1, W2, b2, k=k)
+    b = orc.layer_forward(x[p], Wg, None, W1, b1, W2, b2, k=k)
+    assert np.array_equal(a["y"][p], b["y"])
+    assert np.array_equal(a["idx"][p], b["idx"])
+
+
+# ----------------------------------------------------------------- aux -----
+def test_aux_closed_form(orc):
+    T, E, k = 40, 8, 2
+    L = _rng(11).standard_normal((T, E)).astype(np.float32)
+    L[:, 3] += 3
+    idx, _ = orc.route(L, k)
+    for cap in (T, 6):
+        got = orc.dispatch(idx, E, cap)
+        drops = int((got["slot"] < 0).sum())
+        expect = 0.01 * (T * k - drops) / (T * k * E)
+        assert abs(orc.aux(got["counts"], T, k, 0.01) - expect) <= 1e-17
+    assert abs(orc.aux(orc.dispatch(idx, E, T)["counts"], T, k, 0.01) - 0.01 / E) < 1e-17
+
+
+# ------------------------------------------------------ composed layer -----
+def test_layer_forward_equals_its_parts(orc):
+    from moe_inputs import get, make_inputs
+    c = get("ragged_bf16").scaled(T=120)
+    inp = make_inputs(c)
+    out = orc.layer_forward(inp["x"], inp["Wg"], inp["bg"], inp["W1"], inp["b1"], inp["W2"],
+                            inp["b2"], k=c.k, cf=c.capacity_factor, tau=c.temperature)
+    L = orc.gate(inp["x"], inp["Wg"], inp["bg"])
+    assert np.array_equal(L, out["logits"])
+    idx, w = orc.route(L.astype(np.float32), c.k, c.temperature)
+    cap = orc.capacity(c.T, c.E, c.k, c.capacity_factor)
+    dsp = orc.dispatch(idx, c.E, cap)
+    y = orc.layer_tokens(np.arange(c.T), inp["x"], inp["W1"], inp["b1"], inp["W2"], inp["b2"],
+                         idx, dsp["slot"], w)
+    assert np.array_equal(idx, out["idx"]) and np.array_equal(w, out["w"])
+    for key in ("routed", "counts", "offsets", "perm", "slot"):
+        assert np.array_equal(dsp[key], out[key])
+    assert np.array_equal(y, out["y"])
+    assert (dsp["slot"] < 0).any(), "this case is meant to drop slots"
