@@ -1,0 +1,252 @@
+"""Throughput of the MoE layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+
+A step is one moe_layer_forward call (gate, top-k + softmax, dispatch,
+grouped FFN with the fused weighted combine, counts and balance loss) over
+one batch of seeded synthetic inputs already resident in HBM.  W untimed
+steps, then K timed steps between two device synchronisations on the
+stream the library launches on; per-stage durations come from HIP events
+the library records around each of its launches inside that same timed
+region.  Prints one JSON line.
+
+The default workload is the E=64, top-2, d=2048 layer (T=8192, d_ff=8192,
+capacity factor 2, Zipf-skewed gate).  The oracle (CPU) is timed beside it
+on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer fwd tokens/sec + grouped-GEMM % peak MFMA, E=64 top-2 d=2048"
+PEAK_HBM = 8.0e12          # B/s, MI355X HBM3E
+PEAK_BF16 = 2.5e15         # FLOP/s, dense bf16 matrix
+PEAK_FP32 = 157.3e12       # FLOP/s, fp32
+GEMM_SOURCES = ["mixture_experts_layer_26_amd/csrc/ffn_bf16.hip",
+                "mixture_experts_layer_26_amd/csrc/ffn_sched.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in GEMM_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="budget of the oracle's expert-FFN sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    return ap.parse_args()
+
+
+def stage_bytes_flops(cfg, S, active, esz, nblk):
+    """Algorithmic bytes and FLOPs of each launch (what the method must move
+    or compute over the kept slots; no dense T x E work)."""
+    T, d, E, k, F = cfg.T, cfg.d, cfg.E, cfg.k, cfg.d_ff
+    return {
+        "route": (T * d * esz + d * E * 4 + T * k * 8 + T * d * 4, 2 * T * d * E),
+        "hist": (T * k * 4 + nblk * E * 4, 0),
+        "scatter": (nblk * nblk * E * 4 + T * k * 12 + S * 8, 0),
+        "gather": (2 * S * d * esz, 0),
+        "ffn1": (active * d * F * esz + S * d * esz + S * F * esz + active * F * 4, 2 * S * d * F),
+        "ffn2_combine": (active * F * d * esz + S * F * esz + S * 8 + 2 * S * d * 4 + active * d * 4,
+                         2 * S * d * F),
+    }
+
+
+def cpu_baseline(cfg, inp, budget_s):
+    """Time the oracle (as it stands) on a bounded sample of the workload:
+    gate, routing and dispatch over all tokens, then the expert FFN and
+    combine over leading token chunks until the time budget is spent; the
+    FFN time is scaled to all kept slots."""
+    import numpy as np
+    import oracle
+    x, Wg, bg = inp["x"], inp["Wg"], inp["bg"]
+    t0 = time.perf_counter()
+    L = oracle.gate(x, Wg, bg)
+    idx, w = oracle.route(L.astype(np.float32), cfg.k, cfg.temperature)
+    cap = oracle.capacity(cfg.T, cfg.E, cfg.k, cfg.capacity_factor)
+    dsp = oracle.dispatch(idx, cfg.E, cap)
+    t_route = time.perf_counter() - t0
+    S = int(dsp["offsets"][-1])
+    done_tok, done_slots, t_ffn = 0, 0, 0.0
+    chunk = 64
+    while done_tok < cfg.T and t_ffn < budget_s:
+        toks = np.arange(done_tok, min(cfg.T, done_tok + chunk), dtype=np.int32)
+        t1 = time.perf_counter()
+        oracle.layer_tokens(toks, x, inp["W1"], inp["b1"], inp["W2"], inp["b2"], idx, dsp["slot"], w)
+        t_ffn += time.perf_counter() - t1
+        done_slots += int((dsp["slot"][toks] >= 0).sum())
+        done_tok = int(toks[-1]) + 1
+    total = t_route + t_ffn * (S / max(done_slots, 1))
+    return {
+        "value": cfg.T / total, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+        "sample": (f"gate+top-k+dispatch over all {cfg.T} tokens ({t_route:.2f} s); expert FFN + "
+                   f"combine over the first {done_tok} tokens ({done_slots} of {S} kept slots, "
+                   f"{t_ffn:.2f} s), scaled to all {S} slots; fp64, plain C + OpenMP"),
+        "seconds_measured": round(t_route + t_ffn, 2),
+    }
+
+
+def load_traffic(workload: str, stage: str):
+    p = os.path.join(ROOT, "profiles", f"traffic_{stage}_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import mixture_experts_layer_26_amd as moe
+    from moe_inputs import HEADLINE, get, make_inputs
+
+    cfg = get(args.config or HEADLINE)
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    t_gen = time.perf_counter()
+    inp = make_inputs(cfg)
+
+    def to_dev(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    d = {k: to_dev(v) for k, v in inp.items()}
+    esz = 2 if cfg.dtype == "bf16" else 4
+    s = moe.shape(cfg.T, cfg.d, cfg.E, cfg.k, cfg.d_ff, cfg.capacity_factor, cfg.temperature,
+                  cfg.aux_lambda, moe.MOE_BF16 if cfg.dtype == "bf16" else moe.MOE_F32)
+    ws = moe.workspace(s, dev)
+    y = torch.empty((cfg.T, cfg.d), dtype=torch.float32, device=dev)
+    counts = torch.empty(cfg.E, dtype=torch.int32, device=dev)
+    routed = torch.empty(cfg.E, dtype=torch.int32, device=dev)
+    aux = torch.empty(1, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t_gen
+    stream = torch.cuda.current_stream()
+
+    def step(events=None):
+        if events is not None:
+            moe.moe_set_stage_events(events)
+        moe.moe_layer_forward(s, d["x"], d["Wg"], d["bg"], d["W1"], d["b1"], d["W2"], d["b2"], y,
+                              counts, aux, ws, routed=routed, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    names = moe.moe_stage_names()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(names))]
+          for _ in range(args.steps)]
+    for e in ev:                      # torch creates the HIP event handles lazily on record
+        for x in e:
+            x.record(stream)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(ev[i])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    stage_us = {n: 1e3 * float(np.mean([e[2 * j].elapsed_time(e[2 * j + 1]) for e in ev]))
+                for j, n in enumerate(names)}
+
+    c = counts.cpu().numpy()
+    rt = routed.cpu().numpy()
+    S = int(c.sum())
+    active = int((c > 0).sum())
+    nblk = (cfg.T + (1024 if cfg.E <= 256 else 512 if cfg.E <= 512 else 256) - 1) // \
+        (1024 if cfg.E <= 256 else 512 if cfg.E <= 512 else 256)
+    bf = stage_bytes_flops(cfg, S, active, esz, nblk)
+    ffn_flops = 4 * S * cfg.d * cfg.d_ff
+    gemm_us = stage_us["ffn1"] + stage_us["ffn2_combine"]
+    dom = max(("ffn1", "ffn2_combine"), key=lambda n: stage_us[n])
+    dbytes, dflops = bf[dom]
+    t_dom = stage_us[dom] * 1e-6
+    peak_mm = PEAK_BF16 if esz == 2 else PEAK_FP32
+    hbm_bound = dbytes / PEAK_HBM >= dflops / peak_mm
+    if hbm_bound:
+        roof = {"bound": "hbm", "achieved": dbytes / t_dom / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": dflops / t_dom / 1e12, "peak": peak_mm / 1e12,
+                "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = load_traffic(cfg.name, dom)
+    roof["kernel"] = dom
+    roof["algorithmic_bytes"] = dbytes
+    roof["algorithmic_flops"] = dflops
+    roof["mfma_frac"] = dflops / t_dom / peak_mm
+    roof["hbm_frac"] = dbytes / t_dom / PEAK_HBM
+
+    out = {
+        "metric": METRIC,
+        "value": cfg.T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded numpy PCG64 inputs of the workload's shape and distributions)",
+        "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k,
+                   "d_ff": cfg.d_ff, "capacity_factor": cfg.capacity_factor,
+                   "temperature": cfg.temperature, "seed": cfg.seed,
+                   "gate_bias": (f"zipf s={cfg.zipf_s} alpha={cfg.zipf_alpha}" if cfg.zipf_s else None),
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "grouped_gemm": {"tflops": ffn_flops / (gemm_us * 1e-6) / 1e12,
+                         "frac_peak_bf16": ffn_flops / (gemm_us * 1e-6) / peak_mm, "us": gemm_us},
+        "stages_us": stage_us,
+        "layer_tflops": (ffn_flops + 2 * cfg.T * cfg.d * cfg.E) / (ms * 1e-3) / 1e12,
+        "kept_slots": S, "dropped_slots": cfg.T * cfg.k - S, "active_experts": active,
+        "routed_cv": float(rt.std() / rt.mean()),
+        "aux": float(aux.cpu().numpy()[0]),
+        "setup_seconds": round(t_gen, 2),
+    }
+    if args.copy_calib:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calib_bytes"] = 1 << 30
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

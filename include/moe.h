@@ -1,0 +1,206 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) MoE layer forward library, libmoe.so.
+ *
+ * One GPU's share of a Mixture-of-Experts layer forward:
+ *   gate GEMM -> top-k + softmax -> capacity-limited dispatch into
+ *   expert-contiguous rows -> grouped expert FFN (Linear d->d_ff, exact GELU,
+ *   Linear d_ff->d) -> routing-weighted combine -> per-expert counts and
+ *   balance loss.
+ *
+ * Pages cited (title, then section):
+ *   [PithTrain]  "Native MoE training system PithTrain: core optimisations from
+ *                sparse communication to dynamic memory management"
+ *   [PyTorchMoE] "PyTorch distributed MoE training: principles, implementation
+ *                and optimisation"
+ *   [EP]         "Expert Parallelism: Scaling Mixture-of-Experts Models"
+ *
+ * ---------------------------------------------------------------------------
+ * Conventions shared by every entry point
+ * ---------------------------------------------------------------------------
+ * Pointers.  Every tensor pointer is a DEVICE pointer owned by the caller;
+ *   the library never allocates or frees device memory and keeps no pointer
+ *   after a call returns.  Tensor pointers must be 16-byte aligned.
+ *   `stream` is a hipStream_t (NULL = the default stream).  All calls are
+ *   asynchronous on `stream`; results are valid after the caller synchronises.
+ *   Calls are thread-compatible: concurrent calls need distinct outputs and
+ *   workspaces.
+ * Layouts (all row-major, dense):
+ *   x      [T, d]         dtype            (bf16 = raw uint16 bits, or fp32)
+ *   Wg     [d, E]         fp32
+ *   bg     [E]            fp32, may be NULL (no gate bias)
+ *   W1     [E, d, d_ff]   dtype            expert e: h = x W1[e] + b1[e]
+ *   b1     [E, d_ff]      fp32
+ *   W2     [E, d_ff, d]   dtype            expert e: o = h W2[e] + b2[e]
+ *   b2     [E, d]         fp32
+ *   y      [T, d]         fp32
+ *   logits [T, E]         fp32
+ *   topk_idx [T, k] int32 / topk_w [T, k] fp32: the j-th choice of token t
+ *   routed, counts [E] int32; offsets [E+1] int32
+ *   perm   [max_rows] int32; slot [T, k] int32
+ *   x_perm [max_rows, d] dtype; out_perm [max_rows, d] fp32
+ * Routing semantics (the readings of the pages this library implements):
+ *   - experts are ranked by descending fp32 logit, ties to the LOWER expert
+ *     index (-0 equals +0); topk_idx[t, 0..k-1] is that order;
+ *   - topk_w[t, j] = softmax over the k selected logits divided by
+ *     temperature ([PithTrain] 4.1; [EP] 2.2 for the temperature and the
+ *     hybrid coarse top-8);
+ *   - capacity cap = min(T, ceil(capacity_factor*T*k/E)); capacity_factor <= 0
+ *     means no limit (cap = T) ([PithTrain] 4.3 item 1);
+ *   - slots are kept in token order (t, then j) until an expert holds cap;
+ *     dropped slots contribute nothing and the kept weights are not
+ *     renormalised; a token with every slot dropped gets y = 0;
+ *   - expert e owns rows [offsets[e], offsets[e+1]) of the packed,
+ *     expert-contiguous buffers ([EP] 4.2, the expert bucket pool), in
+ *     increasing token order; S = offsets[E] rows are used;
+ *     max_rows = min(T*k, E*cap).
+ * Precision: the gate accumulates in fp32; the expert GEMMs take bf16 (or
+ *   fp32) operands with fp32 accumulation; bias, GELU, routing weights and
+ *   the combine are fp32; h is stored in the layer dtype (bf16 rounded to
+ *   nearest even) ([EP] 5.5: route in fp32, experts in bf16).
+ * Errors: every entry point validates its arguments on the host first.  On a
+ *   validation failure it returns a non-zero moe_status, launches nothing and
+ *   writes nothing; moe_last_error() then holds a message for the calling
+ *   thread.  A launch failure returns MOE_ERR_HIP.  Faults inside kernels
+ *   surface at the caller's next synchronisation.
+ * Shape limits: T >= 1, 1 <= E <= 1024, 1 <= k <= min(E, 32), d and d_ff
+ *   positive multiples of 8, temperature > 0 and finite, T*k < 2^31.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_NULL = 1,        /* a required pointer is NULL                   */
+    MOE_ERR_SHAPE = 2,       /* shape or hyper-parameter outside the limits  */
+    MOE_ERR_UNSUPPORTED = 3, /* valid request this build does not provide    */
+    MOE_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned      */
+    MOE_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required      */
+    MOE_ERR_HIP = 6          /* a HIP runtime call or launch failed          */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+typedef struct {
+    int64_t T;               /* tokens                                        */
+    int64_t d;               /* model width                                   */
+    int64_t E;               /* experts                                       */
+    int64_t k;               /* experts per token                             */
+    int64_t d_ff;            /* expert hidden width (4d on the pages)         */
+    float capacity_factor;   /* <= 0: no capacity limit                       */
+    float temperature;       /* softmax(l_sel / temperature)                  */
+    float aux_lambda;        /* balance-loss weight lambda                    */
+    int32_t dtype;           /* moe_dtype of x, W1, W2, x_perm and h          */
+} moe_shape;
+
+/* ---- sizes and diagnostics (host only, no device work) ----------------- */
+
+/* Per-expert capacity, min(T, ceil(capacity_factor*T*k/E)), or T without a
+ * limit ([PithTrain] 4.3 item 1).  Returns -1 if the shape is invalid. */
+int64_t moe_capacity(const moe_shape* s);
+
+/* Rows of the expert-contiguous buffers: min(T*k, E*cap).  -1 if invalid. */
+int64_t moe_max_rows(const moe_shape* s);
+
+/* Bytes of workspace every entry point below accepts for this shape (the
+ * largest need, that of moe_layer_forward).  0 if the shape is invalid. */
+size_t moe_workspace_size(const moe_shape* s);
+
+/* Byte offset inside the workspace of an intermediate that
+ * moe_layer_forward leaves there, for inspection after the call completes:
+ * which = MOE_WS_PERM (int32 [max_rows]), MOE_WS_SLOT (int32 [T,k]),
+ * MOE_WS_OFFSETS (int32 [E+1]), MOE_WS_XPERM (dtype [max_rows,d]),
+ * MOE_WS_H (dtype [max_rows,d_ff]).  -1 if invalid. */
+enum { MOE_WS_PERM = 0, MOE_WS_SLOT = 1, MOE_WS_OFFSETS = 2, MOE_WS_XPERM = 3, MOE_WS_H = 4 };
+int64_t moe_workspace_offset(const moe_shape* s, int which);
+
+const char* moe_status_string(int status);
+/* Message of the last failed call on this thread ("" if none). */
+const char* moe_last_error(void);
+/* Library version string. */
+const char* moe_version(void);
+
+/* ---- the hot path ---------------------------------------------------------
+ * 1. Gate + top-k + softmax.  logits[t,e] = sum_i x[t,i] Wg[i,e] + bg[e],
+ *    accumulated in fp32 ([PithTrain] 4.1: linear gate, top-k, softmax over
+ *    the selected values; [PyTorchMoE] 3.2: the gate may carry a bias;
+ *    [EP] 5.5: routing kept in fp32).  Writes topk_idx and topk_w; also the
+ *    logits when `logits` is not NULL. */
+int moe_route(const moe_shape* s, const void* x, const float* Wg, const float* bg,
+              float* logits /* NULL ok */, int32_t* topk_idx, float* topk_w,
+              void* stream);
+
+/* 1b. Top-k + softmax of given fp32 logits [T,E] (same selection and weights
+ *     as moe_route; lets a caller route on logits it already holds). */
+int moe_route_logits(const moe_shape* s, const float* logits, int32_t* topk_idx,
+                     float* topk_w, void* stream);
+
+/* 2. Capacity-limited dispatch ([PithTrain] 4.3 item 1; [EP] 4.1-4.2: rows
+ *    are written straight into their expert's contiguous segment, with no
+ *    concatenation step).  From topk_idx it writes routed[e] (all slots,
+ *    NULL ok), counts[e] (kept slots), offsets[E+1], perm (rows >= S set to
+ *    -1), slot[t,j] (row or -1) and x_perm[row] = x[perm[row]] for row < S
+ *    (rows >= S of x_perm are left as they were).  Each token's k experts
+ *    must be distinct and in [0, E), as moe_route produces them; other
+ *    indices give unspecified (but in-bounds) results. */
+int moe_dispatch(const moe_shape* s, const void* x, const int32_t* topk_idx,
+                 int32_t* routed /* NULL ok */, int32_t* counts, int32_t* offsets,
+                 int32_t* perm, int32_t* slot, void* x_perm,
+                 void* ws, size_t ws_bytes, void* stream);
+
+/* 3. Grouped expert FFN over the packed rows: for every row r of expert e
+ *    (offsets[e] <= r < offsets[e+1]),
+ *      out_perm[r] = GELU(x_perm[r] W1[e] + b1[e]) W2[e] + b2[e]
+ *    with the exact erf GELU ([PithTrain] 4.1 expert = Linear, GELU, Linear;
+ *    [PyTorchMoE] 3.2 Expert with biases).  offsets must be non-decreasing
+ *    with offsets[0] = 0 and offsets[E] <= max_rows.  Rows >= offsets[E] of
+ *    out_perm are not written.  h lives in the workspace. */
+int moe_grouped_ffn(const moe_shape* s, const void* x_perm, const int32_t* offsets,
+                    const void* W1, const float* b1, const void* W2, const float* b2,
+                    float* out_perm, void* ws, size_t ws_bytes, void* stream);
+
+/* 4. Routing-weighted combine back to token order ([PithTrain] 4.1: each
+ *    expert output, scaled by the token's weight for that expert, is added
+ *    into the token's row):  y[t] = sum_{j: slot[t,j] >= 0} topk_w[t,j] *
+ *    out_perm[slot[t,j]], summed in j order.  y is overwritten. */
+int moe_combine(const moe_shape* s, const float* out_perm, const int32_t* slot,
+                const float* topk_w, float* y, void* stream);
+
+/* 5. Balance loss aux = lambda * sum_e (counts[e] / (T k)) * (1/E) with the
+ *    kept counts ([EP] 2.3, taken as printed). */
+int moe_aux_loss(const moe_shape* s, const int32_t* counts, float* aux, void* stream);
+
+/* The whole layer in one call: steps 1-5, with GEMM2's epilogue adding the
+ * weighted rows straight into y (fp32 atomics; y is zeroed inside).  Writes
+ * y, counts and aux; routed, topk_idx, topk_w and logits are optional
+ * outputs (NULL ok).  perm, slot, offsets, x_perm and h stay in the
+ * workspace (see moe_workspace_offset).  Returns like the steps above.
+ * For k <= 2 the result is bitwise reproducible; for k > 2 the order of the
+ * fp32 additions into y may vary between runs. */
+int moe_layer_forward(const moe_shape* s, const void* x, const float* Wg, const float* bg,
+                      const void* W1, const float* b1, const void* W2, const float* b2,
+                      float* y, int32_t* counts, float* aux,
+                      int32_t* routed, int32_t* topk_idx, float* topk_w, float* logits,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* ---- measurement hook ------------------------------------------------------
+ * Stages of moe_layer_forward, in launch order. */
+int moe_num_stages(void);
+const char* moe_stage_name(int i);
+/* Arm per-stage timing for the NEXT moe_layer_forward call on this thread:
+ * events[2i] / events[2i+1] (hipEvent_t, created by the caller; NULL entries
+ * are skipped) are recorded on the call's stream right before / after stage
+ * i.  n_events must be 2*moe_num_stages().  The hook disarms itself after
+ * that one call. */
+int moe_set_stage_events(void** events, int n_events);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

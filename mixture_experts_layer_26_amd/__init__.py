@@ -1,0 +1,199 @@
+"""Python binding of libmoe.so, the gfx950 MoE layer forward.
+
+Argument marshalling only: every function takes torch tensors that already
+live on the GPU, passes their device pointers and the current HIP stream to
+the C ABI of include/moe.h, and raises MoEError on a non-zero status.  Every
+step of the layer runs in the library's HIP kernels; there is no fallback.
+If the library has not been built, importing this package raises.
+
+The names match the C entry points (moe_route, moe_dispatch, ...).
+`layer_forward` is a convenience wrapper that allocates the outputs and the
+workspace with torch and calls moe_layer_forward.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import List, Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build the HIP library first "
+        "(python -m mixture_experts_layer_26_amd.build, or __graft_entry__.build())")
+
+_lib = C.CDLL(LIB_PATH)
+
+MOE_F32, MOE_BF16 = 0, 1
+MOE_WS_PERM, MOE_WS_SLOT, MOE_WS_OFFSETS, MOE_WS_XPERM, MOE_WS_H = range(5)
+
+
+class MoeShape(C.Structure):
+    _fields_ = [("T", C.c_int64), ("d", C.c_int64), ("E", C.c_int64), ("k", C.c_int64),
+                ("d_ff", C.c_int64), ("capacity_factor", C.c_float), ("temperature", C.c_float),
+                ("aux_lambda", C.c_float), ("dtype", C.c_int32)]
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_lib.moe_status_string(status).decode()}: {message}")
+        self.status = status
+
+
+_P = C.c_void_p
+_SP = C.POINTER(MoeShape)
+_Z = C.c_size_t
+_sigs = {
+    "moe_capacity": (C.c_int64, [_SP]),
+    "moe_max_rows": (C.c_int64, [_SP]),
+    "moe_workspace_size": (C.c_size_t, [_SP]),
+    "moe_workspace_offset": (C.c_int64, [_SP, C.c_int]),
+    "moe_status_string": (C.c_char_p, [C.c_int]),
+    "moe_last_error": (C.c_char_p, []),
+    "moe_version": (C.c_char_p, []),
+    "moe_num_stages": (C.c_int, []),
+    "moe_stage_name": (C.c_char_p, [C.c_int]),
+    "moe_set_stage_events": (C.c_int, [C.POINTER(_P), C.c_int]),
+    "moe_route": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_route_logits": (C.c_int, [_SP, _P, _P, _P, _P]),
+    "moe_dispatch": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "moe_grouped_ffn": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "moe_combine": (C.c_int, [_SP, _P, _P, _P, _P, _P]),
+    "moe_aux_loss": (C.c_int, [_SP, _P, _P, _P]),
+    "moe_layer_forward": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                    _P, _Z, _P]),
+}
+for _name, (_res, _args) in _sigs.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+EXPORTS: List[str] = list(_sigs)
+
+
+def shape(T: int, d: int, E: int, k: int, d_ff: int, capacity_factor: float = 0.0,
+          temperature: float = 1.0, aux_lambda: float = 0.01, dtype: int = MOE_BF16) -> MoeShape:
+    return MoeShape(T, d, E, k, d_ff, capacity_factor, temperature, aux_lambda, dtype)
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("tensors passed to libmoe must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libmoe must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise MoEError(rc, _lib.moe_last_error().decode())
+
+
+def moe_capacity(s: MoeShape) -> int:
+    return _lib.moe_capacity(C.byref(s))
+
+
+def moe_max_rows(s: MoeShape) -> int:
+    return _lib.moe_max_rows(C.byref(s))
+
+
+def moe_workspace_size(s: MoeShape) -> int:
+    return _lib.moe_workspace_size(C.byref(s))
+
+
+def moe_workspace_offset(s: MoeShape, which: int) -> int:
+    return _lib.moe_workspace_offset(C.byref(s), which)
+
+
+def moe_version() -> str:
+    return _lib.moe_version().decode()
+
+
+def moe_stage_names() -> List[str]:
+    return [_lib.moe_stage_name(i).decode() for i in range(_lib.moe_num_stages())]
+
+
+def moe_set_stage_events(events: Sequence) -> None:
+    """events: 2 * n_stages torch.cuda.Event (or None), created with enable_timing."""
+    arr = (_P * len(events))(*[None if e is None else e.cuda_event for e in events])
+    _check(_lib.moe_set_stage_events(arr, len(events)))
+
+
+def moe_route(s, x, Wg, bg, logits, topk_idx, topk_w, stream=None) -> None:
+    _check(_lib.moe_route(C.byref(s), _ptr(x), _ptr(Wg), _ptr(bg), _ptr(logits), _ptr(topk_idx),
+                          _ptr(topk_w), _stream(stream)))
+
+
+def moe_route_logits(s, logits, topk_idx, topk_w, stream=None) -> None:
+    _check(_lib.moe_route_logits(C.byref(s), _ptr(logits), _ptr(topk_idx), _ptr(topk_w),
+                                 _stream(stream)))
+
+
+def moe_dispatch(s, x, topk_idx, routed, counts, offsets, perm, slot, x_perm, ws,
+                 stream=None) -> None:
+    _check(_lib.moe_dispatch(C.byref(s), _ptr(x), _ptr(topk_idx), _ptr(routed), _ptr(counts),
+                             _ptr(offsets), _ptr(perm), _ptr(slot), _ptr(x_perm), _ptr(ws),
+                             ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_grouped_ffn(s, x_perm, offsets, W1, b1, W2, b2, out_perm, ws, stream=None) -> None:
+    _check(_lib.moe_grouped_ffn(C.byref(s), _ptr(x_perm), _ptr(offsets), _ptr(W1), _ptr(b1),
+                                _ptr(W2), _ptr(b2), _ptr(out_perm), _ptr(ws),
+                                ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_combine(s, out_perm, slot, topk_w, y, stream=None) -> None:
+    _check(_lib.moe_combine(C.byref(s), _ptr(out_perm), _ptr(slot), _ptr(topk_w), _ptr(y),
+                            _stream(stream)))
+
+
+def moe_aux_loss(s, counts, aux, stream=None) -> None:
+    _check(_lib.moe_aux_loss(C.byref(s), _ptr(counts), _ptr(aux), _stream(stream)))
+
+
+def moe_layer_forward(s, x, Wg, bg, W1, b1, W2, b2, y, counts, aux, ws, routed=None,
+                      topk_idx=None, topk_w=None, logits=None, stream=None) -> None:
+    _check(_lib.moe_layer_forward(C.byref(s), _ptr(x), _ptr(Wg), _ptr(bg), _ptr(W1), _ptr(b1),
+                                  _ptr(W2), _ptr(b2), _ptr(y), _ptr(counts), _ptr(aux),
+                                  _ptr(routed), _ptr(topk_idx), _ptr(topk_w), _ptr(logits),
+                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def workspace(s: MoeShape, device="cuda"):
+    import torch
+    n = moe_workspace_size(s)
+    if n == 0:
+        raise MoEError(2, _lib.moe_last_error().decode())
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def layer_forward(x, Wg, bg, W1, b1, W2, b2, k: int = 2, capacity_factor: float = 0.0,
+                  temperature: float = 1.0, aux_lambda: float = 0.01, ws=None):
+    """(y, counts, aux) of the MoE layer; x, W1, W2 are bf16 bit patterns
+    stored as torch.int16/uint16/bfloat16, or float32 tensors."""
+    import torch
+    T, d = x.shape
+    E = Wg.shape[1]
+    d_ff = W1.shape[2]
+    dt = MOE_F32 if x.dtype == torch.float32 else MOE_BF16
+    s = shape(T, d, E, k, d_ff, capacity_factor, temperature, aux_lambda, dt)
+    if ws is None:
+        ws = workspace(s, x.device)
+    y = torch.empty((T, d), dtype=torch.float32, device=x.device)
+    counts = torch.empty(E, dtype=torch.int32, device=x.device)
+    aux = torch.empty(1, dtype=torch.float32, device=x.device)
+    moe_layer_forward(s, x, Wg, bg, W1, b1, W2, b2, y, counts, aux, ws)
+    return y, counts, aux

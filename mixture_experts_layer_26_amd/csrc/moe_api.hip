@@ -1,0 +1,474 @@
+// moe_api.hip -- the C ABI of libmoe.so (declared in include/moe.h).
+//
+// Host side only: argument validation (before any launch), workspace
+// carve-up, and the launch sequence of each entry point on the caller's
+// stream.  No device memory is allocated here and no host synchronisation
+// happens on the hot path.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "../../include/moe.h"
+#include "moe_kernels.h"
+
+namespace moe {
+
+static thread_local std::string g_err;
+static thread_local std::vector<hipEvent_t> g_events;
+static thread_local bool g_events_armed = false;
+
+static int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int device_cu_count() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+            n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+struct Geo {
+    int64_t T, d, E, k, dff, cap, max_rows;
+    int esz;      // bytes per element of x / W / h
+    int BT, nblk; // dispatch token blocks
+};
+
+// cap = min(T, ceil(cf * T * k / E)); cf <= 0: no limit.  cf*T*k is exact in
+// double for T*k < 2^29; the ceiling is settled with integer-valued products.
+static int64_t capacity_of(int64_t T, int64_t E, int64_t k, float cf) {
+    if (!(cf > 0.0f)) return T;
+    const double q = (double)cf * (double)T * (double)k;
+    int64_t c = (int64_t)std::ceil(q / (double)E);
+    while (c > 1 && (double)(c - 1) * (double)E >= q) --c;
+    while ((double)c * (double)E < q) ++c;
+    return c < T ? c : T;
+}
+
+static int validate(const moe_shape* s, Geo* g) {
+    if (s == nullptr) return fail(MOE_ERR_NULL, "shape is NULL");
+    if (s->T < 1) return fail(MOE_ERR_SHAPE, "T must be >= 1 (got %lld)", (long long)s->T);
+    if (s->E < 1 || s->E > 1024) return fail(MOE_ERR_SHAPE, "E must be in [1, 1024] (got %lld)", (long long)s->E);
+    if (s->k < 1 || s->k > s->E || s->k > 32)
+        return fail(MOE_ERR_SHAPE, "k must be in [1, min(E, 32)] (got k=%lld, E=%lld)", (long long)s->k,
+                    (long long)s->E);
+    if (s->d < 8 || s->d % 8 != 0) return fail(MOE_ERR_SHAPE, "d must be a positive multiple of 8 (got %lld)", (long long)s->d);
+    if (s->d_ff < 8 || s->d_ff % 8 != 0)
+        return fail(MOE_ERR_SHAPE, "d_ff must be a positive multiple of 8 (got %lld)", (long long)s->d_ff);
+    if (!(s->temperature > 0.0f) || !std::isfinite(s->temperature))
+        return fail(MOE_ERR_SHAPE, "temperature must be finite and > 0");
+    if (!std::isfinite(s->capacity_factor)) return fail(MOE_ERR_SHAPE, "capacity_factor must be finite");
+    if (!std::isfinite(s->aux_lambda)) return fail(MOE_ERR_SHAPE, "aux_lambda must be finite");
+    if (s->dtype != MOE_F32 && s->dtype != MOE_BF16) return fail(MOE_ERR_SHAPE, "dtype must be MOE_F32 or MOE_BF16");
+    if (s->T * s->k >= (int64_t(1) << 31)) return fail(MOE_ERR_SHAPE, "T*k must be < 2^31");
+    if (s->d > (1 << 20) || s->d_ff > (1 << 20)) return fail(MOE_ERR_SHAPE, "d and d_ff must be <= 2^20");
+    if (g) {
+        g->T = s->T;
+        g->d = s->d;
+        g->E = s->E;
+        g->k = s->k;
+        g->dff = s->d_ff;
+        g->cap = capacity_of(s->T, s->E, s->k, s->capacity_factor);
+        g->max_rows = std::min(s->T * s->k, s->E * g->cap);
+        g->esz = s->dtype == MOE_BF16 ? 2 : 4;
+        g->BT = dispatch_block_tokens((int)s->E);
+        g->nblk = (int)((s->T + g->BT - 1) / g->BT);
+    }
+    return MOE_OK;
+}
+
+struct WsLayout {
+    size_t blkhist, offsets, idx, w, perm, slot, roww, xperm, h, total;
+};
+
+static size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
+
+static WsLayout ws_layout(const Geo& g) {
+    WsLayout L{};
+    size_t p = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = p;
+        p = align_up(p + (bytes ? bytes : 1));
+        return at;
+    };
+    L.blkhist = take(sizeof(int32_t) * (size_t)g.nblk * g.E);
+    L.offsets = take(sizeof(int32_t) * (size_t)(g.E + 1));
+    L.idx = take(sizeof(int32_t) * (size_t)(g.T * g.k));
+    L.w = take(sizeof(float) * (size_t)(g.T * g.k));
+    L.perm = take(sizeof(int32_t) * (size_t)g.max_rows);
+    L.slot = take(sizeof(int32_t) * (size_t)(g.T * g.k));
+    L.roww = take(sizeof(float) * (size_t)g.max_rows);
+    L.xperm = take((size_t)g.esz * (size_t)g.max_rows * g.d);
+    L.h = take((size_t)g.esz * (size_t)g.max_rows * g.dff);
+    L.total = p;
+    return L;
+}
+
+static bool misaligned(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+#define MOE_REQUIRE(ptr)                                                        \
+    do {                                                                        \
+        if ((ptr) == nullptr) return fail(MOE_ERR_NULL, "%s is NULL", #ptr);   \
+        if (misaligned(ptr)) return fail(MOE_ERR_ALIGN, "%s is not 16-byte aligned", #ptr); \
+    } while (0)
+#define MOE_OPTIONAL(ptr)                                                       \
+    do {                                                                        \
+        if (misaligned(ptr)) return fail(MOE_ERR_ALIGN, "%s is not 16-byte aligned", #ptr); \
+    } while (0)
+#define MOE_HIP(call, what)                                                     \
+    do {                                                                        \
+        hipError_t e_ = (call);                                                 \
+        if (e_ != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e_)); \
+    } while (0)
+
+static int check_ws(const Geo& g, void* ws, size_t ws_bytes, WsLayout* L) {
+    *L = ws_layout(g);
+    if (ws == nullptr) return fail(MOE_ERR_WORKSPACE, "workspace is NULL");
+    if (misaligned(ws)) return fail(MOE_ERR_ALIGN, "workspace is not 16-byte aligned");
+    if (ws_bytes < L->total)
+        return fail(MOE_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, L->total);
+    return MOE_OK;
+}
+
+template <typename T>
+static T* at(void* ws, size_t off) {
+    return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+static const char* kStageNames[] = {"route", "hist", "scatter", "gather", "ffn1", "ffn2_combine"};
+constexpr int kNumStages = 6;
+
+static void stage_event(int stage, int after, hipStream_t st) {
+    if (!g_events_armed) return;
+    const size_t i = 2 * (size_t)stage + after;
+    if (i < g_events.size() && g_events[i] != nullptr) (void)hipEventRecord(g_events[i], st);
+}
+
+static DispatchArgs dispatch_args(const Geo& g, const moe_shape* s) {
+    DispatchArgs a{};
+    a.T = g.T;
+    a.E = (int)g.E;
+    a.k = (int)g.k;
+    a.cap = g.cap;
+    a.max_rows = g.max_rows;
+    a.BT = g.BT;
+    a.nblk = g.nblk;
+    a.lambda = s->aux_lambda;
+    a.row_bytes = g.d * g.esz;
+    return a;
+}
+
+static hipError_t launch_gemm(const Geo& g, const GemmArgs& ga, int epi, hipStream_t st) {
+    return g.esz == 2 ? launch_ffn_gemm_bf16(ga, epi, st) : launch_ffn_gemm_f32(ga, epi, st);
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int64_t moe_capacity(const moe_shape* s) {
+    Geo g;
+    if (validate(s, &g) != MOE_OK) return -1;
+    return g.cap;
+}
+
+int64_t moe_max_rows(const moe_shape* s) {
+    Geo g;
+    if (validate(s, &g) != MOE_OK) return -1;
+    return g.max_rows;
+}
+
+size_t moe_workspace_size(const moe_shape* s) {
+    Geo g;
+    if (validate(s, &g) != MOE_OK) return 0;
+    return ws_layout(g).total;
+}
+
+int64_t moe_workspace_offset(const moe_shape* s, int which) {
+    Geo g;
+    if (validate(s, &g) != MOE_OK) return -1;
+    const WsLayout L = ws_layout(g);
+    switch (which) {
+        case MOE_WS_PERM: return (int64_t)L.perm;
+        case MOE_WS_SLOT: return (int64_t)L.slot;
+        case MOE_WS_OFFSETS: return (int64_t)L.offsets;
+        case MOE_WS_XPERM: return (int64_t)L.xperm;
+        case MOE_WS_H: return (int64_t)L.h;
+        default: fail(MOE_ERR_SHAPE, "unknown workspace region %d", which); return -1;
+    }
+}
+
+const char* moe_status_string(int status) {
+    switch (status) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_NULL: return "MOE_ERR_NULL";
+        case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE";
+        case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+        case MOE_ERR_ALIGN: return "MOE_ERR_ALIGN";
+        case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+        case MOE_ERR_HIP: return "MOE_ERR_HIP";
+        default: return "MOE_ERR_UNKNOWN";
+    }
+}
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+const char* moe_version(void) { return "moe-mi355x 0.1 (gfx950)"; }
+
+int moe_num_stages(void) { return kNumStages; }
+
+const char* moe_stage_name(int i) { return (i >= 0 && i < kNumStages) ? kStageNames[i] : ""; }
+
+int moe_set_stage_events(void** events, int n_events) {
+    if (events == nullptr) return fail(MOE_ERR_NULL, "events is NULL");
+    if (n_events != 2 * kNumStages)
+        return fail(MOE_ERR_SHAPE, "n_events must be %d (got %d)", 2 * kNumStages, n_events);
+    g_events.assign(reinterpret_cast<hipEvent_t*>(events), reinterpret_cast<hipEvent_t*>(events) + n_events);
+    g_events_armed = true;
+    return MOE_OK;
+}
+
+int moe_route(const moe_shape* s, const void* x, const float* Wg, const float* bg, float* logits,
+              int32_t* topk_idx, float* topk_w, void* stream) {
+    Geo g;
+    if (int rc = validate(s, &g)) return rc;
+    MOE_REQUIRE(x);
+    MOE_REQUIRE(Wg);
+    MOE_OPTIONAL(bg);
+    MOE_OPTIONAL(logits);
+    MOE_REQUIRE(topk_idx);
+    MOE_REQUIRE(topk_w);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    RouteArgs a = route_config(g.T, (int)g.d, (int)g.E, (int)g.k, s->temperature);
+    a.x = x;
+    a.Wg = Wg;
+    a.bg = bg;
+    a.logits = logits;
+    a.idx = topk_idx;
+    a.w = topk_w;
+    MOE_HIP(launch_route_gate(a, s->dtype, st), "route kernel launch");
+    return MOE_OK;
+}
+
+int moe_route_logits(const moe_shape* s, const float* logits, int32_t* topk_idx, float* topk_w,
+                     void* stream) {
+    Geo g;
+    if (int rc = validate(s, &g)) return rc;
+    MOE_REQUIRE(logits);
+    MOE_REQUIRE(topk_idx);
+    MOE_REQUIRE(topk_w);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    RouteArgs a = route_config(g.T, (int)g.d, (int)g.E, (int)g.k, s->temperature);
+    a.logits = const_cast<float*>(logits);
+    a.idx = topk_idx;
+    a.w = topk_w;
+    MOE_HIP(launch_route_logits(a, st), "route_logits kernel launch");
+    return MOE_OK;
+}
+
+int moe_dispatch(const moe_shape* s, const void* x, const int32_t* topk_idx, int32_t* routed,
+                 int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* slot, void* x_perm,
+                 void* ws, size_t ws_bytes, void* stream) {
+    Geo g;
+    if (int rc = validate(s, &g)) return rc;
+    MOE_REQUIRE(x);
+    MOE_REQUIRE(topk_idx);
+    MOE_OPTIONAL(routed);
+    MOE_REQUIRE(counts);
+    MOE_REQUIRE(offsets);
+    MOE_REQUIRE(perm);
+    MOE_REQUIRE(slot);
+    MOE_REQUIRE(x_perm);
+    WsLayout L;
+    if (int rc = check_ws(g, ws, ws_bytes, &L)) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    DispatchArgs a = dispatch_args(g, s);
+    a.idx = topk_idx;
+    a.blkhist = at<int32_t>(ws, L.blkhist);
+    a.routed = routed;
+    a.counts = counts;
+    a.offsets = offsets;
+    a.perm = perm;
+    a.slot = slot;
+    a.x = x;
+    a.x_perm = x_perm;
+    MOE_HIP(launch_hist(a, st), "hist kernel launch");
+    MOE_HIP(launch_scatter(a, st), "scatter kernel launch");
+    MOE_HIP(launch_gather(a, st), "gather kernel launch");
+    return MOE_OK;
+}
+
+int moe_grouped_ffn(const moe_shape* s, const void* x_perm, const int32_t* offsets, const void* W1,
+                    const float* b1, const void* W2, const float* b2, float* out_perm, void* ws,
+                    size_t ws_bytes, void* stream) {
+    Geo g;
+    if (int rc = validate(s, &g)) return rc;
+    MOE_REQUIRE(x_perm);
+    MOE_REQUIRE(offsets);
+    MOE_REQUIRE(W1);
+    MOE_REQUIRE(b1);
+    MOE_REQUIRE(W2);
+    MOE_REQUIRE(b2);
+    MOE_REQUIRE(out_perm);
+    WsLayout L;
+    if (int rc = check_ws(g, ws, ws_bytes, &L)) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    GemmArgs g1{};
+    g1.A = x_perm;
+    g1.B = W1;
+    g1.bias = b1;
+    g1.offsets = offsets;
+    g1.E = (int)g.E;
+    g1.K = (int)g.d;
+    g1.N = (int)g.dff;
+    g1.out = at<void>(ws, L.h);
+    MOE_HIP(launch_gemm(g, g1, EPI_GELU_H, st), "ffn1 kernel launch");
+    GemmArgs g2 = g1;
+    g2.A = g1.out;
+    g2.B = W2;
+    g2.bias = b2;
+    g2.K = (int)g.dff;
+    g2.N = (int)g.d;
+    g2.out = out_perm;
+    MOE_HIP(launch_gemm(g, g2, EPI_STORE_F32, st), "ffn2 kernel launch");
+    return MOE_OK;
+}
+
+int moe_combine(const moe_shape* s, const float* out_perm, const int32_t* slot, const float* topk_w,
+                float* y, void* stream) {
+    Geo g;
+    if (int rc = validate(s, &g)) return rc;
+    MOE_REQUIRE(out_perm);
+    MOE_REQUIRE(slot);
+    MOE_REQUIRE(topk_w);
+    MOE_REQUIRE(y);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    MOE_HIP(launch_combine(g.T, (int)g.d, (int)g.k, out_perm, slot, topk_w, y, st), "combine kernel launch");
+    return MOE_OK;
+}
+
+int moe_aux_loss(const moe_shape* s, const int32_t* counts, float* aux, void* stream) {
+    Geo g;
+    if (int rc = validate(s, &g)) return rc;
+    MOE_REQUIRE(counts);
+    MOE_REQUIRE(aux);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    MOE_HIP(launch_aux((int)g.E, g.T, (int)g.k, s->aux_lambda, counts, aux, st), "aux kernel launch");
+    return MOE_OK;
+}
+
+int moe_layer_forward(const moe_shape* s, const void* x, const float* Wg, const float* bg, const void* W1,
+                      const float* b1, const void* W2, const float* b2, float* y, int32_t* counts,
+                      float* aux, int32_t* routed, int32_t* topk_idx, float* topk_w, float* logits,
+                      void* ws, size_t ws_bytes, void* stream) {
+    struct Disarm {
+        ~Disarm() { g_events_armed = false; }
+    } disarm;
+    Geo g;
+    if (int rc = validate(s, &g)) return rc;
+    MOE_REQUIRE(x);
+    MOE_REQUIRE(Wg);
+    MOE_OPTIONAL(bg);
+    MOE_REQUIRE(W1);
+    MOE_REQUIRE(b1);
+    MOE_REQUIRE(W2);
+    MOE_REQUIRE(b2);
+    MOE_REQUIRE(y);
+    MOE_REQUIRE(counts);
+    MOE_REQUIRE(aux);
+    MOE_OPTIONAL(routed);
+    MOE_OPTIONAL(topk_idx);
+    MOE_OPTIONAL(topk_w);
+    MOE_OPTIONAL(logits);
+    WsLayout L;
+    if (int rc = check_ws(g, ws, ws_bytes, &L)) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int32_t* idx = topk_idx ? topk_idx : at<int32_t>(ws, L.idx);
+    float* w = topk_w ? topk_w : at<float>(ws, L.w);
+
+    // 1. gate + top-k + softmax; also zeroes y for the fused combine
+    RouteArgs ra = route_config(g.T, (int)g.d, (int)g.E, (int)g.k, s->temperature);
+    ra.x = x;
+    ra.Wg = Wg;
+    ra.bg = bg;
+    ra.logits = logits;
+    ra.idx = idx;
+    ra.w = w;
+    ra.yzero = y;
+    ra.ycols = g.d;
+    stage_event(0, 0, st);
+    MOE_HIP(launch_route_gate(ra, s->dtype, st), "route kernel launch");
+    stage_event(0, 1, st);
+
+    // 2. dispatch
+    DispatchArgs da = dispatch_args(g, s);
+    da.idx = idx;
+    da.w = w;
+    da.blkhist = at<int32_t>(ws, L.blkhist);
+    da.routed = routed;
+    da.counts = counts;
+    da.offsets = at<int32_t>(ws, L.offsets);
+    da.perm = at<int32_t>(ws, L.perm);
+    da.slot = at<int32_t>(ws, L.slot);
+    da.row_w = at<float>(ws, L.roww);
+    da.aux = aux;
+    da.x = x;
+    da.x_perm = at<void>(ws, L.xperm);
+    stage_event(1, 0, st);
+    MOE_HIP(launch_hist(da, st), "hist kernel launch");
+    stage_event(1, 1, st);
+    stage_event(2, 0, st);
+    MOE_HIP(launch_scatter(da, st), "scatter kernel launch");
+    stage_event(2, 1, st);
+    stage_event(3, 0, st);
+    MOE_HIP(launch_gather(da, st), "gather kernel launch");
+    stage_event(3, 1, st);
+
+    // 3. grouped FFN; GEMM2 adds w * (h W2 + b2) into y
+    GemmArgs g1{};
+    g1.A = da.x_perm;
+    g1.B = W1;
+    g1.bias = b1;
+    g1.offsets = da.offsets;
+    g1.E = (int)g.E;
+    g1.K = (int)g.d;
+    g1.N = (int)g.dff;
+    g1.out = at<void>(ws, L.h);
+    stage_event(4, 0, st);
+    MOE_HIP(launch_gemm(g, g1, EPI_GELU_H, st), "ffn1 kernel launch");
+    stage_event(4, 1, st);
+    GemmArgs g2 = g1;
+    g2.A = g1.out;
+    g2.B = W2;
+    g2.bias = b2;
+    g2.K = (int)g.dff;
+    g2.N = (int)g.d;
+    g2.out = y;
+    g2.perm = da.perm;
+    g2.row_w = da.row_w;
+    stage_event(5, 0, st);
+    MOE_HIP(launch_gemm(g, g2, EPI_COMBINE, st), "ffn2 kernel launch");
+    stage_event(5, 1, st);
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,73 @@
+// moe_common.h -- device helpers shared by the gfx950 kernels of libmoe.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+#define MOE_LDS __attribute__((address_space(3)))
+
+namespace moe {
+
+constexpr int kWave = 64;
+constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, round-robin WG dispatch
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+    return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// fp32 -> bf16, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// Exact-erf GELU in fp32: u * Phi(u) = 0.5 u (1 + erf(u / sqrt 2)), using the
+// device library's erff.
+__device__ __forceinline__ float gelu_erf(float u) {
+    return 0.5f * u * (1.0f + erff(u * 0.70710678118654752440f));
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+// Inclusive prefix sum over the threads of a block (blockDim.x <= 1024),
+// `tmp` is __shared__ scratch of at least 32 ints.  Every thread must call it.
+__device__ __forceinline__ int block_inclusive_scan(int v, int* tmp) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wid = threadIdx.x / kWave;
+    const int nw = (blockDim.x + kWave - 1) / kWave;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        int o = __shfl_up(v, off, kWave);
+        if (lane >= off) v += o;
+    }
+    if (lane == kWave - 1) tmp[wid] = v;
+    __syncthreads();
+    if (wid == 0) {
+        int s = (lane < nw) ? tmp[lane] : 0;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            int o = __shfl_up(s, off, kWave);
+            if (lane >= off) s += o;
+        }
+        if (lane < nw) tmp[lane] = s;
+    }
+    __syncthreads();
+    if (wid > 0) v += tmp[wid - 1];
+    __syncthreads();
+    return v;
+}
+
+}  // namespace moe

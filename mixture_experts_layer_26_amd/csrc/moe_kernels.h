@@ -1,0 +1,82 @@
+// moe_kernels.h -- argument blocks and launchers of the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---- route.hip ----------------------------------------------------------
+struct RouteArgs {
+    int64_t T;
+    int d, E, k;
+    float tau;
+    const void* x;       // [T, d] bf16 bits or fp32
+    const float* Wg;     // [d, E]
+    const float* bg;     // [E] or null
+    float* logits;       // [T, E] or null (gate kernel: optional output; logits kernel: input)
+    int32_t* idx;        // [T, k]
+    float* w;            // [T, k]
+    float* yzero;        // [T, ycols] rows zeroed by the gate kernel, or null
+    int64_t ycols;
+    int TB, Epad, KC, G;  // launch geometry, from route_config()
+};
+RouteArgs route_config(int64_t T, int d, int E, int k, float tau);
+size_t route_smem_bytes(const RouteArgs& a);
+hipError_t launch_route_gate(const RouteArgs& a, int dtype, hipStream_t st);
+hipError_t launch_route_logits(const RouteArgs& a, hipStream_t st);
+
+// ---- dispatch.hip -------------------------------------------------------
+struct DispatchArgs {
+    int64_t T;
+    int E, k;
+    int64_t cap, max_rows;
+    int BT, nblk;          // token block of the histogram / scatter kernels
+    const int32_t* idx;    // [T, k]
+    const float* w;        // [T, k] or null
+    int32_t* blkhist;      // [nblk, E] workspace
+    int32_t* routed;       // [E] or null
+    int32_t* counts;       // [E] or null
+    int32_t* offsets;      // [E+1]
+    int32_t* perm;         // [max_rows]
+    int32_t* slot;         // [T, k]
+    float* row_w;          // [max_rows] or null
+    float* aux;            // [1] or null
+    float lambda;
+    // gather
+    const void* x;         // [T, d]
+    void* x_perm;          // [max_rows, d]
+    int64_t row_bytes;     // d * element size
+};
+int dispatch_block_tokens(int E);
+hipError_t launch_hist(const DispatchArgs& a, hipStream_t st);
+hipError_t launch_scatter(const DispatchArgs& a, hipStream_t st);
+hipError_t launch_gather(const DispatchArgs& a, hipStream_t st);
+
+// ---- ffn_bf16.hip / ffn_fp32.hip ----------------------------------------
+enum { EPI_GELU_H = 0, EPI_STORE_F32 = 1, EPI_COMBINE = 2 };
+struct GemmArgs {
+    const void* A;           // [rows, K], row-major, layer dtype
+    const void* B;           // [E, K, N], row-major, layer dtype
+    const float* bias;       // [E, N]
+    const int32_t* offsets;  // [E+1] row segments of the experts
+    int E, K, N;
+    void* out;               // EPI_GELU_H: [rows, N] dtype; EPI_STORE_F32: [rows, N] fp32;
+                             // EPI_COMBINE: y [T, N] fp32
+    const int32_t* perm;     // EPI_COMBINE: token of each row
+    const float* row_w;      // EPI_COMBINE: routing weight of each row
+};
+hipError_t launch_ffn_gemm_bf16(const GemmArgs& g, int epi, hipStream_t st);
+hipError_t launch_ffn_gemm_f32(const GemmArgs& g, int epi, hipStream_t st);
+
+// ---- combine.hip ----------------------------------------------------------
+hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t st);
+hipError_t launch_combine(int64_t T, int d, int k, const float* out_perm, const int32_t* slot,
+                          const float* w, float* y, hipStream_t st);
+hipError_t launch_aux(int E, int64_t T, int k, float lambda, const int32_t* counts, float* aux,
+                      hipStream_t st);
+
+// device properties (moe_api.hip)
+int device_cu_count();
+
+}  // namespace moe

@@ -114,6 +114,12 @@ _add(MoEConfig("cap_one", T=200, d=64, E=8, k=2, d_ff=64,
                capacity_factor=0.02, bias_std=0.1,
                note="capacity clips to 1 slot per expert"))
 
+# limits of the library: E = 1024 experts, k = 32 choices per token
+_add(MoEConfig("max_experts", T=2048, d=64, E=1024, k=4, d_ff=64,
+               capacity_factor=1.0, bias_std=0.1))
+_add(MoEConfig("max_k", T=256, d=64, E=48, k=32, d_ff=64,
+               capacity_factor=0.0, temperature=2.0, bias_std=0.1))
+
 # The workload the throughput metric is quoted on (E=64, top-2, d=2048).
 HEADLINE = "skewed_e64"
 # The five workloads in their published order.

@@ -1,0 +1,150 @@
+"""GPU checks of the properties the method fixes at any size: tie-breaking
+of the selection, identity experts, closed-form dispatch, dropped tokens,
+run-to-run determinism and the invariants of the routing outputs."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import gpu_harness as H
+from moe_inputs import bf16_bits_to_f32, f32_to_bf16_bits, get, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def moe():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    import mixture_experts_layer_26_amd as m
+    return m
+
+
+@pytest.mark.parametrize("E,k,tau", [(8, 2, 1.0), (16, 3, 0.7), (64, 2, 1.0), (100, 7, 0.2),
+                                     (128, 8, 0.2), (256, 2, 1.0), (1000, 5, 1.5), (1024, 32, 1.0)])
+def test_route_logits_ties(moe, orc, E, k, tau):
+    import torch
+    r = np.random.default_rng(E * 100 + k)
+    T = 777
+    L = r.integers(-3, 4, (T, E)).astype(np.float32)       # many exact ties
+    L[r.random((T, E)) < 0.1] = -0.0
+    L[::5] = r.standard_normal((len(L[::5]), E)).astype(np.float32)
+    L[3] = 0.5                                              # all tied
+    s = moe.shape(T, 64, E, k, 64, 0.0, tau)
+    idx = H.empty((T, k), torch.int32)
+    w = H.empty((T, k), torch.float32)
+    moe.moe_route_logits(s, H.to_dev(L), idx, w)
+    torch.cuda.synchronize()
+    idx_ref, w_ref = orc.route(L, k, tau)
+    assert np.array_equal(H.to_host(idx), idx_ref)
+    assert np.abs(H.to_host(w) - w_ref).max() <= H.TOL_W
+    assert list(H.to_host(idx)[3]) == list(range(k))
+
+
+def _identity(E, d, dff, dtype):
+    W1 = np.zeros((E, d, dff), np.float32)
+    W2 = np.zeros((E, dff, d), np.float32)
+    I = np.eye(d, dtype=np.float32)
+    W1[:, :, :d], W1[:, :, d:2 * d] = I, -I
+    W2[:, :d, :], W2[:, d:2 * d, :] = I, -I
+    if dtype == "bf16":
+        W1, W2 = f32_to_bf16_bits(W1), f32_to_bf16_bits(W2)
+    return W1, W2
+
+
+@pytest.mark.parametrize("dtype,tol", [("bf16", 1e-2), ("fp32", 1e-5)])
+def test_identity_experts_reproduce_x(moe, dtype, tol):
+    """GELU(u) - GELU(-u) = u, so experts [I | -I | 0] then [I; -I; 0] return x
+    and, with no capacity limit, y = x (up to the rounding of h)."""
+    import torch
+    T, d, dff, E, k = 1500, 128, 512, 8, 2
+    r = np.random.default_rng(3)
+    x = r.standard_normal((T, d)).astype(np.float32)
+    xs = f32_to_bf16_bits(x) if dtype == "bf16" else x
+    Wg = (r.standard_normal((d, E)) / np.sqrt(d)).astype(np.float32)
+    W1, W2 = _identity(E, d, dff, dtype)
+    b1 = np.zeros((E, dff), np.float32)
+    b2 = np.zeros((E, d), np.float32)
+    y, counts, aux = moe.layer_forward(H.to_dev(xs), H.to_dev(Wg), None, H.to_dev(W1), H.to_dev(b1),
+                                       H.to_dev(W2), H.to_dev(b2), k=k)
+    torch.cuda.synchronize()
+    xref = bf16_bits_to_f32(xs) if dtype == "bf16" else x
+    H.assert_close_norm(H.to_host(y), xref, tol, f"identity experts {dtype}")
+    assert int(H.to_host(counts).sum()) == T * k
+
+
+def test_dispatch_closed_form_two_experts(moe):
+    """Every token prefers experts 0 then 1 and each keeps cap = c slots: the
+    first c tokens are kept on both, 2 (T - c) slots are dropped."""
+    import torch
+    T, E, k, d = 3000, 6, 2, 64
+    cf = 0.6  # cap = ceil(0.6 * 3000 * 2 / 6) = 600
+    s = moe.shape(T, d, E, k, 64, cf)
+    c = moe.moe_capacity(s)
+    assert c == 600
+    L = np.full((T, E), -1.0, np.float32)
+    L[:, 0], L[:, 1] = 2.0, 1.0
+    idx = H.empty((T, k), torch.int32)
+    w = H.empty((T, k), torch.float32)
+    moe.moe_route_logits(s, H.to_dev(L), idx, w)
+    x = H.to_dev(f32_to_bf16_bits(np.random.default_rng(0).standard_normal((T, d)).astype(np.float32)))
+    smax = moe.moe_max_rows(s)
+    counts, routed = H.empty(E, torch.int32), H.empty(E, torch.int32)
+    offsets, perm = H.empty(E + 1, torch.int32), H.empty(smax, torch.int32)
+    slot = H.empty((T, k), torch.int32)
+    xperm = H.empty((smax, d), torch.int16)
+    moe.moe_dispatch(s, x, idx, routed, counts, offsets, perm, slot, xperm, moe.workspace(s))
+    torch.cuda.synchronize()
+    sl = H.to_host(slot)
+    assert int((sl < 0).sum()) == 2 * (T - c)
+    assert H.to_host(counts).tolist() == [c, c, 0, 0, 0, 0]
+    assert H.to_host(routed).tolist() == [T, T, 0, 0, 0, 0]
+    p = H.to_host(perm)
+    assert np.array_equal(p[:c], np.arange(c)) and np.array_equal(p[c:2 * c], np.arange(c))
+    assert (p[2 * c:] == -1).all()
+    assert np.array_equal(sl[:c, 0], np.arange(c)) and np.array_equal(sl[:c, 1], c + np.arange(c))
+
+
+@pytest.mark.parametrize("name", ["cap_one", "ragged_bf16", "bf16_e16", "hybrid_small"])
+def test_invariants_and_determinism(moe, name):
+    """k distinct experts, weights sum to 1, counts sum to T*k - drops, the
+    permutation is a bijection onto kept slots, fully dropped tokens give 0,
+    and repeated calls give identical integers (and identical y for k <= 2)."""
+    import torch
+    cfg = get(name)
+    inp = make_inputs(cfg)
+    dv = H.dev_inputs(inp)
+    s = H.make_shape(moe, cfg)
+    T, E, k = cfg.T, cfg.E, cfg.k
+    ws = moe.workspace(s)
+    outs = []
+    for rep in range(2):
+        y = H.empty((T, cfg.d), torch.float32)
+        counts, aux = H.empty(E, torch.int32), H.empty(1, torch.float32)
+        idx, w = H.empty((T, k), torch.int32), H.empty((T, k), torch.float32)
+        moe.moe_layer_forward(s, dv["x"], dv["Wg"], dv["bg"], dv["W1"], dv["b1"], dv["W2"], dv["b2"],
+                              y, counts, aux, ws, topk_idx=idx, topk_w=w)
+        torch.cuda.synchronize()
+        wsh = H.to_host(ws)
+        so = moe.moe_workspace_offset(s, moe.MOE_WS_SLOT)
+        po = moe.moe_workspace_offset(s, moe.MOE_WS_PERM)
+        slot = wsh[so:so + 4 * T * k].view(np.int32).reshape(T, k).copy()
+        perm = wsh[po:po + 4 * moe.moe_max_rows(s)].view(np.int32).copy()
+        outs.append((H.to_host(y), H.to_host(counts), H.to_host(idx), H.to_host(w), slot, perm))
+    y, counts, idx, w, slot, perm = outs[0]
+    assert all(len(set(r)) == k for r in idx.tolist())
+    assert np.abs(w.sum(1) - 1.0).max() <= 1e-6
+    drops = int((slot < 0).sum())
+    S = int(counts.sum())
+    assert S == T * k - drops
+    assert np.array_equal(np.sort(slot[slot >= 0]), np.arange(S))
+    tt, jj = np.nonzero(slot >= 0)
+    assert np.array_equal(perm[slot[tt, jj]], tt)
+    dead = (slot < 0).all(1)
+    assert (y[dead] == 0).all()
+    for a, b in zip(outs[0][1:], outs[1][1:]):
+        assert np.array_equal(a, b)
+    if k <= 2:
+        assert np.array_equal(outs[0][0], outs[1][0]), "y not bitwise reproducible for k <= 2"
+    else:
+        H.assert_close_norm(outs[1][0], outs[0][0], 1e-6, f"{name} repeat y")
