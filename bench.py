@@ -3,7 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
 
 A step is one moe_layer_forward call (gate, top-k + softmax, dispatch,
-grouped FFN with the fused weighted combine, counts and balance loss) over
+grouped FFN, weighted combine, counts and balance loss) over
 one batch of seeded synthetic inputs already resident in HBM.  W untimed
 steps, then K timed steps between two device synchronisations on the
 stream the library launches on; per-stage durations come from HIP events
@@ -32,7 +32,8 @@ PEAK_HBM = 8.0e12          # B/s, MI355X HBM3E
 PEAK_BF16 = 2.5e15         # FLOP/s, dense bf16 matrix
 PEAK_FP32 = 157.3e12       # FLOP/s, fp32
 GEMM_SOURCES = ["mixture_experts_layer_26_amd/csrc/ffn_bf16.hip",
-                "mixture_experts_layer_26_amd/csrc/ffn_sched.h"]
+                "mixture_experts_layer_26_amd/csrc/ffn_sched.h",
+                "mixture_experts_layer_26_amd/csrc/moe_common.h"]
 
 
 def kernel_source_hash() -> str:
@@ -67,8 +68,8 @@ def stage_bytes_flops(cfg, S, active, esz, nblk):
         "scatter": (nblk * nblk * E * 4 + T * k * 12 + S * 8, 0),
         "gather": (2 * S * d * esz, 0),
         "ffn1": (active * d * F * esz + S * d * esz + S * F * esz + active * F * 4, 2 * S * d * F),
-        "ffn2_combine": (active * F * d * esz + S * F * esz + S * 8 + 2 * S * d * 4 + active * d * 4,
-                         2 * S * d * F),
+        "ffn2": (active * F * d * esz + S * F * esz + S * d * 4 + active * d * 4, 2 * S * d * F),
+        "combine": (S * d * 4 + T * d * 4 + T * k * 8, 2 * S * d),
     }
 
 
@@ -189,8 +190,8 @@ def main():
         (1024 if cfg.E <= 256 else 512 if cfg.E <= 512 else 256)
     bf = stage_bytes_flops(cfg, S, active, esz, nblk)
     ffn_flops = 4 * S * cfg.d * cfg.d_ff
-    gemm_us = stage_us["ffn1"] + stage_us["ffn2_combine"]
-    dom = max(("ffn1", "ffn2_combine"), key=lambda n: stage_us[n])
+    gemm_us = stage_us["ffn1"] + stage_us["ffn2"]
+    dom = max(stage_us, key=lambda n: stage_us[n])
     dbytes, dflops = bf[dom]
     t_dom = stage_us[dom] * 1e-6
     peak_mm = PEAK_BF16 if esz == 2 else PEAK_FP32

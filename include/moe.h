@@ -63,7 +63,8 @@
  *   thread.  A launch failure returns MOE_ERR_HIP.  Faults inside kernels
  *   surface at the caller's next synchronisation.
  * Shape limits: T >= 1, 1 <= E <= 1024, 1 <= k <= min(E, 32), d and d_ff
- *   positive multiples of 8, temperature > 0 and finite, T*k < 2^31.
+ *   positive multiples of 8 with d * d_ff <= 2^29, temperature > 0 and
+ *   finite, T*k < 2^31.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -116,8 +117,10 @@ size_t moe_workspace_size(const moe_shape* s);
  * moe_layer_forward leaves there, for inspection after the call completes:
  * which = MOE_WS_PERM (int32 [max_rows]), MOE_WS_SLOT (int32 [T,k]),
  * MOE_WS_OFFSETS (int32 [E+1]), MOE_WS_XPERM (dtype [max_rows,d]),
- * MOE_WS_H (dtype [max_rows,d_ff]).  -1 if invalid. */
-enum { MOE_WS_PERM = 0, MOE_WS_SLOT = 1, MOE_WS_OFFSETS = 2, MOE_WS_XPERM = 3, MOE_WS_H = 4 };
+ * MOE_WS_H (dtype [max_rows,d_ff]), MOE_WS_OUT (fp32 [max_rows,d], the
+ * expert outputs before the weighted sum).  -1 if invalid. */
+enum { MOE_WS_PERM = 0, MOE_WS_SLOT = 1, MOE_WS_OFFSETS = 2, MOE_WS_XPERM = 3, MOE_WS_H = 4,
+       MOE_WS_OUT = 5 };
 int64_t moe_workspace_offset(const moe_shape* s, int which);
 
 const char* moe_status_string(int status);
@@ -176,13 +179,12 @@ int moe_combine(const moe_shape* s, const float* out_perm, const int32_t* slot,
  *    kept counts ([EP] 2.3, taken as printed). */
 int moe_aux_loss(const moe_shape* s, const int32_t* counts, float* aux, void* stream);
 
-/* The whole layer in one call: steps 1-5, with GEMM2's epilogue adding the
- * weighted rows straight into y (fp32 atomics; y is zeroed inside).  Writes
- * y, counts and aux; routed, topk_idx, topk_w and logits are optional
- * outputs (NULL ok).  perm, slot, offsets, x_perm and h stay in the
- * workspace (see moe_workspace_offset).  Returns like the steps above.
- * For k <= 2 the result is bitwise reproducible; for k > 2 the order of the
- * fp32 additions into y may vary between runs. */
+/* The whole layer in one call: steps 1-5 on one stream (the balance loss is
+ * produced by the dispatch step).  Writes y, counts and aux; routed,
+ * topk_idx, topk_w and logits are optional outputs (NULL ok).  perm, slot,
+ * offsets, x_perm, h and the expert outputs stay in the workspace (see
+ * moe_workspace_offset).  Returns like the steps above.  The result is
+ * bitwise reproducible: no step depends on the order of atomic updates. */
 int moe_layer_forward(const moe_shape* s, const void* x, const float* Wg, const float* bg,
                       const void* W1, const float* b1, const void* W2, const float* b2,
                       float* y, int32_t* counts, float* aux,

@@ -27,7 +27,7 @@ if not os.path.exists(LIB_PATH):
 _lib = C.CDLL(LIB_PATH)
 
 MOE_F32, MOE_BF16 = 0, 1
-MOE_WS_PERM, MOE_WS_SLOT, MOE_WS_OFFSETS, MOE_WS_XPERM, MOE_WS_H = range(5)
+MOE_WS_PERM, MOE_WS_SLOT, MOE_WS_OFFSETS, MOE_WS_XPERM, MOE_WS_H, MOE_WS_OUT = range(6)
 
 
 class MoeShape(C.Structure):

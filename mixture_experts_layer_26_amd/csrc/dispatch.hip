@@ -13,7 +13,7 @@
 //             kept totals and the offsets; the in-block rank of a slot is a
 //             popcount over a per-expert bitmask of the block's tokens (a
 //             token holds each expert at most once), so ranks follow token
-//             order exactly;  kept slots write perm / slot / row weight;
+//             order exactly;  kept slots write perm and slot;
 //             block 0 also writes routed, counts, offsets and the balance
 //             loss ([EP] section 2.3);
 //   gather  : x_perm[row] = x[perm[row]] with 16-byte vector copies, one
@@ -125,7 +125,6 @@ __global__ __launch_bounds__(1024) void scatter_kernel(DispatchArgs a) {
                 if (p < a.cap) {
                     row = off_s[e] + (int)p;
                     a.perm[row] = (int32_t)t;
-                    if (a.row_w) a.row_w[row] = a.w[s];
                 }
             }
             a.slot[s] = row;

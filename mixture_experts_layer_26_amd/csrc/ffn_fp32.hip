@@ -85,17 +85,9 @@ __global__ __launch_bounds__(256) void ffn_gemm_f32_kernel(GemmArgs g) {
             if constexpr (EPI == EPI_GELU_H) {
                 *reinterpret_cast<float4*>(static_cast<float*>(g.out) + row * N + n) =
                     make_float4(gelu_erf(v0), gelu_erf(v1), gelu_erf(v2), gelu_erf(v3));
-            } else if constexpr (EPI == EPI_STORE_F32) {
+            } else {
                 *reinterpret_cast<float4*>(static_cast<float*>(g.out) + row * N + n) =
                     make_float4(v0, v1, v2, v3);
-            } else {
-                const int64_t t = g.perm[row];
-                const float wt = g.row_w[row];
-                float* yp = static_cast<float*>(g.out) + t * N + n;
-                atomicAdd(yp + 0, wt * v0);
-                atomicAdd(yp + 1, wt * v1);
-                atomicAdd(yp + 2, wt * v2);
-                atomicAdd(yp + 3, wt * v3);
             }
         }
     }
@@ -117,20 +109,12 @@ static int persistent_grid_f32() {
 }
 
 hipError_t launch_ffn_gemm_f32(const GemmArgs& g, int epi, hipStream_t st) {
-    switch (epi) {
-        case EPI_GELU_H:
-            hipLaunchKernelGGL(ffn_gemm_f32_kernel<EPI_GELU_H>, dim3(persistent_grid_f32<EPI_GELU_H>()),
-                               dim3(256), 0, st, g);
-            break;
-        case EPI_STORE_F32:
-            hipLaunchKernelGGL(ffn_gemm_f32_kernel<EPI_STORE_F32>,
-                               dim3(persistent_grid_f32<EPI_STORE_F32>()), dim3(256), 0, st, g);
-            break;
-        default:
-            hipLaunchKernelGGL(ffn_gemm_f32_kernel<EPI_COMBINE>,
-                               dim3(persistent_grid_f32<EPI_COMBINE>()), dim3(256), 0, st, g);
-            break;
-    }
+    if (epi == EPI_GELU_H)
+        hipLaunchKernelGGL(ffn_gemm_f32_kernel<EPI_GELU_H>, dim3(persistent_grid_f32<EPI_GELU_H>()), dim3(256), 0,
+                           st, g);
+    else
+        hipLaunchKernelGGL(ffn_gemm_f32_kernel<EPI_STORE_F32>, dim3(persistent_grid_f32<EPI_STORE_F32>()),
+                           dim3(256), 0, st, g);
     return hipGetLastError();
 }
 

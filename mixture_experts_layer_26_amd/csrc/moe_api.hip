@@ -13,7 +13,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/moe.h"
+#include "moe.h"
 #include "moe_kernels.h"
 
 namespace moe {
@@ -79,6 +79,8 @@ static int validate(const moe_shape* s, Geo* g) {
     if (s->dtype != MOE_F32 && s->dtype != MOE_BF16) return fail(MOE_ERR_SHAPE, "dtype must be MOE_F32 or MOE_BF16");
     if (s->T * s->k >= (int64_t(1) << 31)) return fail(MOE_ERR_SHAPE, "T*k must be < 2^31");
     if (s->d > (1 << 20) || s->d_ff > (1 << 20)) return fail(MOE_ERR_SHAPE, "d and d_ff must be <= 2^20");
+    // one expert matrix must stay below 2^30 elements (32-bit byte offsets in the GEMMs)
+    if (s->d * s->d_ff > (int64_t(1) << 29)) return fail(MOE_ERR_SHAPE, "d * d_ff must be <= 2^29");
     if (g) {
         g->T = s->T;
         g->d = s->d;
@@ -95,7 +97,7 @@ static int validate(const moe_shape* s, Geo* g) {
 }
 
 struct WsLayout {
-    size_t blkhist, offsets, idx, w, perm, slot, roww, xperm, h, total;
+    size_t blkhist, offsets, idx, w, perm, slot, xperm, h, out, total;
 };
 
 static size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
@@ -114,9 +116,9 @@ static WsLayout ws_layout(const Geo& g) {
     L.w = take(sizeof(float) * (size_t)(g.T * g.k));
     L.perm = take(sizeof(int32_t) * (size_t)g.max_rows);
     L.slot = take(sizeof(int32_t) * (size_t)(g.T * g.k));
-    L.roww = take(sizeof(float) * (size_t)g.max_rows);
     L.xperm = take((size_t)g.esz * (size_t)g.max_rows * g.d);
     L.h = take((size_t)g.esz * (size_t)g.max_rows * g.dff);
+    L.out = take(sizeof(float) * (size_t)g.max_rows * g.d);
     L.total = p;
     return L;
 }
@@ -152,8 +154,8 @@ static T* at(void* ws, size_t off) {
     return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
 
-static const char* kStageNames[] = {"route", "hist", "scatter", "gather", "ffn1", "ffn2_combine"};
-constexpr int kNumStages = 6;
+static const char* kStageNames[] = {"route", "hist", "scatter", "gather", "ffn1", "ffn2", "combine"};
+constexpr int kNumStages = 7;
 
 static void stage_event(int stage, int after, hipStream_t st) {
     if (!g_events_armed) return;
@@ -176,7 +178,7 @@ static DispatchArgs dispatch_args(const Geo& g, const moe_shape* s) {
 }
 
 static hipError_t launch_gemm(const Geo& g, const GemmArgs& ga, int epi, hipStream_t st) {
-    return g.esz == 2 ? launch_ffn_gemm_bf16(ga, epi, st) : launch_ffn_gemm_f32(ga, epi, st);
+    return g.esz == 2 ? launch_ffn_gemm_bf16(ga, epi, g.max_rows, st) : launch_ffn_gemm_f32(ga, epi, st);
 }
 
 }  // namespace moe
@@ -213,6 +215,7 @@ int64_t moe_workspace_offset(const moe_shape* s, int which) {
         case MOE_WS_OFFSETS: return (int64_t)L.offsets;
         case MOE_WS_XPERM: return (int64_t)L.xperm;
         case MOE_WS_H: return (int64_t)L.h;
+        case MOE_WS_OUT: return (int64_t)L.out;
         default: fail(MOE_ERR_SHAPE, "unknown workspace region %d", which); return -1;
     }
 }
@@ -258,7 +261,7 @@ int moe_route(const moe_shape* s, const void* x, const float* Wg, const float* b
     MOE_REQUIRE(topk_idx);
     MOE_REQUIRE(topk_w);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    RouteArgs a = route_config(g.T, (int)g.d, (int)g.E, (int)g.k, s->temperature);
+    RouteArgs a = route_config(g.T, (int)g.d, (int)g.E, (int)g.k, s->temperature, s->dtype, device_cu_count());
     a.x = x;
     a.Wg = Wg;
     a.bg = bg;
@@ -277,7 +280,7 @@ int moe_route_logits(const moe_shape* s, const float* logits, int32_t* topk_idx,
     MOE_REQUIRE(topk_idx);
     MOE_REQUIRE(topk_w);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    RouteArgs a = route_config(g.T, (int)g.d, (int)g.E, (int)g.k, s->temperature);
+    RouteArgs a = route_config(g.T, (int)g.d, (int)g.E, (int)g.k, s->temperature, s->dtype, device_cu_count());
     a.logits = const_cast<float*>(logits);
     a.idx = topk_idx;
     a.w = topk_w;
@@ -405,16 +408,14 @@ int moe_layer_forward(const moe_shape* s, const void* x, const float* Wg, const 
     int32_t* idx = topk_idx ? topk_idx : at<int32_t>(ws, L.idx);
     float* w = topk_w ? topk_w : at<float>(ws, L.w);
 
-    // 1. gate + top-k + softmax; also zeroes y for the fused combine
-    RouteArgs ra = route_config(g.T, (int)g.d, (int)g.E, (int)g.k, s->temperature);
+    // 1. gate + top-k + softmax
+    RouteArgs ra = route_config(g.T, (int)g.d, (int)g.E, (int)g.k, s->temperature, s->dtype, device_cu_count());
     ra.x = x;
     ra.Wg = Wg;
     ra.bg = bg;
     ra.logits = logits;
     ra.idx = idx;
     ra.w = w;
-    ra.yzero = y;
-    ra.ycols = g.d;
     stage_event(0, 0, st);
     MOE_HIP(launch_route_gate(ra, s->dtype, st), "route kernel launch");
     stage_event(0, 1, st);
@@ -422,14 +423,12 @@ int moe_layer_forward(const moe_shape* s, const void* x, const float* Wg, const 
     // 2. dispatch
     DispatchArgs da = dispatch_args(g, s);
     da.idx = idx;
-    da.w = w;
     da.blkhist = at<int32_t>(ws, L.blkhist);
     da.routed = routed;
     da.counts = counts;
     da.offsets = at<int32_t>(ws, L.offsets);
     da.perm = at<int32_t>(ws, L.perm);
     da.slot = at<int32_t>(ws, L.slot);
-    da.row_w = at<float>(ws, L.roww);
     da.aux = aux;
     da.x = x;
     da.x_perm = at<void>(ws, L.xperm);
@@ -443,7 +442,7 @@ int moe_layer_forward(const moe_shape* s, const void* x, const float* Wg, const 
     MOE_HIP(launch_gather(da, st), "gather kernel launch");
     stage_event(3, 1, st);
 
-    // 3. grouped FFN; GEMM2 adds w * (h W2 + b2) into y
+    // 3. grouped FFN over the expert-contiguous rows
     GemmArgs g1{};
     g1.A = da.x_perm;
     g1.B = W1;
@@ -462,12 +461,16 @@ int moe_layer_forward(const moe_shape* s, const void* x, const float* Wg, const 
     g2.bias = b2;
     g2.K = (int)g.dff;
     g2.N = (int)g.d;
-    g2.out = y;
-    g2.perm = da.perm;
-    g2.row_w = da.row_w;
+    g2.out = at<float>(ws, L.out);
     stage_event(5, 0, st);
-    MOE_HIP(launch_gemm(g, g2, EPI_COMBINE, st), "ffn2 kernel launch");
+    MOE_HIP(launch_gemm(g, g2, EPI_STORE_F32, st), "ffn2 kernel launch");
     stage_event(5, 1, st);
+
+    // 4. weighted sum back to token order (overwrites y)
+    stage_event(6, 0, st);
+    MOE_HIP(launch_combine(g.T, (int)g.d, (int)g.k, at<float>(ws, L.out), da.slot, w, y, st),
+            "combine kernel launch");
+    stage_event(6, 1, st);
     return MOE_OK;
 }
 

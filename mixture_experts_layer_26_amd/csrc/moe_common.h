@@ -4,7 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/moe.h"
+#include "moe.h"
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
@@ -33,6 +33,28 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 // device library's erff.
 __device__ __forceinline__ float gelu_erf(float u) {
     return 0.5f * u * (1.0f + erff(u * 0.70710678118654752440f));
+}
+
+// GELU through the erf approximation of Abramowitz & Stegun, Handbook of
+// Mathematical Functions, eq. 7.1.26: for z >= 0,
+//   erfc(z) = (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-z^2) + eps,
+//   t = 1 / (1 + p z),  |eps| <= 1.5e-7.
+// With z = |u| / sqrt 2, q = erfc(z) / 2 = Phi(-|u|) and
+//   GELU(u) = u (1 - q) for u >= 0,  u q for u < 0,
+// which keeps GELU(u) - GELU(-u) = u and a small relative error in the
+// negative tail.  Used where h is rounded to bf16 (8 mantissa bits), far
+// coarser than this error.
+__device__ __forceinline__ float gelu_as(float u) {
+    const float z = fabsf(u) * 0.70710678118654752440f;
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
+    float poly = fmaf(t, 1.061405429f, -1.453152027f);
+    poly = fmaf(t, poly, 1.421413741f);
+    poly = fmaf(t, poly, -0.284496736f);
+    poly = fmaf(t, poly, 0.254829592f);
+    poly *= t;
+    const float e = __builtin_amdgcn_exp2f(-z * z * 1.44269504088896340736f);  // exp(-z^2)
+    const float q = 0.5f * poly * e;
+    return u * (u >= 0.0f ? 1.0f - q : q);
 }
 
 template <typename T>

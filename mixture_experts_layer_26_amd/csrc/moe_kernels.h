@@ -17,11 +17,10 @@ struct RouteArgs {
     float* logits;       // [T, E] or null (gate kernel: optional output; logits kernel: input)
     int32_t* idx;        // [T, k]
     float* w;            // [T, k]
-    float* yzero;        // [T, ycols] rows zeroed by the gate kernel, or null
-    int64_t ycols;
     int TB, Epad, KC, G;  // launch geometry, from route_config()
+    int MR, lkv, lep;     // micro-tile rows, log2(KC / vector), log2(padded E)
 };
-RouteArgs route_config(int64_t T, int d, int E, int k, float tau);
+RouteArgs route_config(int64_t T, int d, int E, int k, float tau, int dtype, int cus);
 size_t route_smem_bytes(const RouteArgs& a);
 hipError_t launch_route_gate(const RouteArgs& a, int dtype, hipStream_t st);
 hipError_t launch_route_logits(const RouteArgs& a, hipStream_t st);
@@ -33,14 +32,12 @@ struct DispatchArgs {
     int64_t cap, max_rows;
     int BT, nblk;          // token block of the histogram / scatter kernels
     const int32_t* idx;    // [T, k]
-    const float* w;        // [T, k] or null
     int32_t* blkhist;      // [nblk, E] workspace
     int32_t* routed;       // [E] or null
     int32_t* counts;       // [E] or null
     int32_t* offsets;      // [E+1]
     int32_t* perm;         // [max_rows]
     int32_t* slot;         // [T, k]
-    float* row_w;          // [max_rows] or null
     float* aux;            // [1] or null
     float lambda;
     // gather
@@ -54,19 +51,16 @@ hipError_t launch_scatter(const DispatchArgs& a, hipStream_t st);
 hipError_t launch_gather(const DispatchArgs& a, hipStream_t st);
 
 // ---- ffn_bf16.hip / ffn_fp32.hip ----------------------------------------
-enum { EPI_GELU_H = 0, EPI_STORE_F32 = 1, EPI_COMBINE = 2 };
+enum { EPI_GELU_H = 0, EPI_STORE_F32 = 1 };
 struct GemmArgs {
     const void* A;           // [rows, K], row-major, layer dtype
     const void* B;           // [E, K, N], row-major, layer dtype
     const float* bias;       // [E, N]
     const int32_t* offsets;  // [E+1] row segments of the experts
     int E, K, N;
-    void* out;               // EPI_GELU_H: [rows, N] dtype; EPI_STORE_F32: [rows, N] fp32;
-                             // EPI_COMBINE: y [T, N] fp32
-    const int32_t* perm;     // EPI_COMBINE: token of each row
-    const float* row_w;      // EPI_COMBINE: routing weight of each row
+    void* out;               // EPI_GELU_H: [rows, N] dtype; EPI_STORE_F32: [rows, N] fp32
 };
-hipError_t launch_ffn_gemm_bf16(const GemmArgs& g, int epi, hipStream_t st);
+hipError_t launch_ffn_gemm_bf16(const GemmArgs& g, int epi, int64_t max_rows, hipStream_t st);
 hipError_t launch_ffn_gemm_f32(const GemmArgs& g, int epi, hipStream_t st);
 
 // ---- combine.hip ----------------------------------------------------------

@@ -8,23 +8,16 @@
 //
 // One workgroup owns TB tokens.  Phase 1 accumulates the [TB x E] logit tile
 // in fp32 on the vector ALUs (x and Wg staged through LDS in K-chunks, each
-// thread a 4x4 register tile).  Phase 2 hands each token to a group of G
+// thread an MR x 4 register tile).  Phase 2 hands each token to a group of G
 // lanes (G = E rounded up to a power of two, at most 64); each lane keeps
 // ceil(E/G) logits in registers and k rounds of butterfly arg-max (shuffle
 // xor) pick the winners, ties to the lower expert index.
 #include "moe_common.h"
 #include "moe_kernels.h"
 
-namespace moe {
+#include <algorithm>
 
-template <typename XT>
-__device__ __forceinline__ float load_x(const XT* p, int64_t i);
-template <>
-__device__ __forceinline__ float load_x<float>(const float* p, int64_t i) { return p[i]; }
-template <>
-__device__ __forceinline__ float load_x<uint16_t>(const uint16_t* p, int64_t i) {
-    return bf16_bits_to_f32(p[i]);
-}
+namespace moe {
 
 __device__ __forceinline__ bool beats(float av, int ai, float bv, int bi) {
     return av > bv || (av == bv && ai < bi);
@@ -83,56 +76,128 @@ __device__ __forceinline__ void topk_softmax_group(const float* row, int E, int 
     }
 }
 
-template <typename XT, int NV>
+// Phase 1 geometry (host: route_config): thread (tq, eq) owns an MR x 4
+// block of the [TB x E] logit tile; each K-chunk of x (16-byte vectors) and of
+// Wg (scalars, rows padded to EP2 = 2^lep) is loaded into registers one chunk
+// ahead of its use, so global latency overlaps the FMAs of the previous chunk.
+constexpr int kMaxXV = 4;    // 16-byte x vectors per thread per K-chunk
+constexpr int kMaxWS = 32;   // Wg scalars per thread per K-chunk
+
+template <typename XT>
+__device__ __forceinline__ void unpack16(const uint4& v, float* o);
+template <>
+__device__ __forceinline__ void unpack16<float>(const uint4& v, float* o) {
+    o[0] = __uint_as_float(v.x);
+    o[1] = __uint_as_float(v.y);
+    o[2] = __uint_as_float(v.z);
+    o[3] = __uint_as_float(v.w);
+}
+template <>
+__device__ __forceinline__ void unpack16<uint16_t>(const uint4& v, float* o) {
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        o[2 * i] = __uint_as_float(u[i] << 16);
+        o[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+    }
+}
+
+template <typename XT, int MR, int NV>
 __global__ __launch_bounds__(256) void route_gate_topk_kernel(RouteArgs a) {
     extern __shared__ __attribute__((aligned(16))) float smem[];
+    constexpr int VEC = 16 / sizeof(XT);
     const int TB = a.TB, Epad = a.Epad, KC = a.KC, KCP = a.KC + 1, LTP = a.Epad + 1;
-    float* xs = smem;              // [TB][KCP]
-    float* wsm = xs + TB * KCP;    // [KC][Epad]
-    float* lt = wsm + KC * Epad;   // [TB][LTP]
+    const int EP2 = 1 << a.lep;
+    float* xs = smem;                          // [TB][KCP]
+    float* wsm = xs + ((TB * KCP + 3) & ~3);   // [KC][EP2], 16-byte aligned
+    float* lt = wsm + KC * EP2;    // [TB][LTP]
     const XT* __restrict__ x = static_cast<const XT*>(a.x);
     const int64_t T = a.T;
     const int d = a.d, E = a.E;
     const int64_t t0 = (int64_t)blockIdx.x * TB;
     const int tid = threadIdx.x;
-    const int n_eq = Epad / 4, n_tq = TB / 4;
+    const int n_eq = Epad / 4, n_tq = TB / MR;
     const int tq = tid / n_eq, eq = tid % n_eq;
     const bool comp = tid < n_eq * n_tq;
+    const int lkv = a.lkv;                 // log2(KC / VEC)
+    const int nxv = TB << lkv;             // x vectors per chunk
+    const int nws = KC << a.lep;           // Wg scalars per chunk
 
-    float acc[4][4];
+    float acc[MR][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MR; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
 
+    uint4 xr[kMaxXV];
+    float wr[kMaxWS];
+    auto load = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < kMaxXV; ++i) {
+            const int v = tid + 256 * i;
+            if (v < nxv) {
+                const int tt = v >> lkv, kv = v & ((1 << lkv) - 1);
+                const int64_t t = t0 + tt;
+                const int kg = k0 + kv * VEC;
+                xr[i] = (t < T && kg < d) ? *reinterpret_cast<const uint4*>(x + t * d + kg)
+                                          : make_uint4(0u, 0u, 0u, 0u);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kMaxWS; ++j) {
+            const int i = tid + 256 * j;
+            if (i < nws) {
+                const int kk = i >> a.lep, e = i & (EP2 - 1);
+                const int kg = k0 + kk;
+                wr[j] = (kg < d && e < E) ? a.Wg[(int64_t)kg * E + e] : 0.0f;
+            }
+        }
+    };
+    auto store = [&]() {
+#pragma unroll
+        for (int i = 0; i < kMaxXV; ++i) {
+            const int v = tid + 256 * i;
+            if (v < nxv) {
+                const int tt = v >> lkv, kv = v & ((1 << lkv) - 1);
+                float f[VEC];
+                unpack16<XT>(xr[i], f);
+#pragma unroll
+                for (int q = 0; q < VEC; ++q) xs[tt * KCP + kv * VEC + q] = f[q];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kMaxWS; ++j) {
+            const int i = tid + 256 * j;
+            if (i < nws) wsm[i] = wr[j];
+        }
+    };
+
+    load(0);
     for (int k0 = 0; k0 < d; k0 += KC) {
-        for (int i = tid; i < TB * KC; i += blockDim.x) {
-            const int tt = i / KC, kk = i - tt * KC;
-            const int64_t t = t0 + tt;
-            const int kg = k0 + kk;
-            xs[tt * KCP + kk] = (t < T && kg < d) ? load_x<XT>(x, t * d + kg) : 0.0f;
-        }
-        for (int i = tid; i < KC * Epad; i += blockDim.x) {
-            const int kk = i / Epad, e = i - kk * Epad;
-            const int kg = k0 + kk;
-            wsm[i] = (kg < d && e < E) ? a.Wg[(int64_t)kg * E + e] : 0.0f;
-        }
+        store();
         __syncthreads();
+        if (k0 + KC < d) load(k0 + KC);
         if (comp) {
             const int kmax = min(KC, d - k0);
-            for (int kk = 0; kk < kmax; ++kk) {
-                const float4 wv = *reinterpret_cast<const float4*>(&wsm[kk * Epad + 4 * eq]);
-                float xv[4];
+            auto step = [&](int kk) {
+                const float4 wv = *reinterpret_cast<const float4*>(&wsm[kk * EP2 + 4 * eq]);
+                float xv[MR];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) xv[i] = xs[(4 * tq + i) * KCP + kk];
+                for (int i = 0; i < MR; ++i) xv[i] = xs[(MR * tq + i) * KCP + kk];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
+                for (int i = 0; i < MR; ++i) {
                     acc[i][0] = fmaf(xv[i], wv.x, acc[i][0]);
                     acc[i][1] = fmaf(xv[i], wv.y, acc[i][1]);
                     acc[i][2] = fmaf(xv[i], wv.z, acc[i][2]);
                     acc[i][3] = fmaf(xv[i], wv.w, acc[i][3]);
                 }
+            };
+            int kk = 0;
+            for (; kk + 8 <= kmax; kk += 8) {   // batches the LDS reads of 8 steps
+#pragma unroll
+                for (int u = 0; u < 8; ++u) step(kk + u);
             }
+            for (; kk < kmax; ++kk) step(kk);
         }
         __syncthreads();
     }
@@ -142,7 +207,7 @@ __global__ __launch_bounds__(256) void route_gate_topk_kernel(RouteArgs a) {
             const int e = 4 * eq + j;
             const float b = (a.bg != nullptr && e < E) ? a.bg[e] : 0.0f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) lt[(4 * tq + i) * LTP + e] = acc[i][j] + b;
+            for (int i = 0; i < MR; ++i) lt[(MR * tq + i) * LTP + e] = acc[i][j] + b;
         }
     }
     __syncthreads();
@@ -165,13 +230,6 @@ __global__ __launch_bounds__(256) void route_gate_topk_kernel(RouteArgs a) {
         const float* row = lt + (active ? tt : 0) * LTP;
         topk_softmax_group<NV>(row, E, a.k, a.tau, G, gl, active, a.idx + (active ? t : 0) * a.k,
                                a.w + (active ? t : 0) * a.k);
-    }
-    // zero this block's rows of y (the fused combine adds into it later)
-    if (a.yzero != nullptr) {
-        const int64_t nrow = min((int64_t)TB, T - t0);
-        const int64_t n4 = nrow * a.ycols / 4;
-        float4* yz = reinterpret_cast<float4*>(a.yzero + t0 * a.ycols);
-        for (int64_t i = tid; i < n4; i += blockDim.x) yz[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
 }
 
@@ -197,7 +255,13 @@ static int route_nv(int E, int G) {
     return nv <= 1 ? 1 : nv <= 2 ? 2 : nv <= 4 ? 4 : nv <= 8 ? 8 : 16;
 }
 
-RouteArgs route_config(int64_t T, int d, int E, int k, float tau) {
+static int ilog2(int v) {
+    int l = 0;
+    while ((1 << l) < v) ++l;
+    return l;
+}
+
+RouteArgs route_config(int64_t T, int d, int E, int k, float tau, int dtype, int cus) {
     RouteArgs a{};
     a.T = T;
     a.d = d;
@@ -205,36 +269,52 @@ RouteArgs route_config(int64_t T, int d, int E, int k, float tau) {
     a.k = k;
     a.tau = tau;
     a.Epad = (E + 3) & ~3;
+    a.lep = ilog2(a.Epad);
+    const int EP2 = 1 << a.lep;
     const int n_eq = a.Epad / 4;
-    int tb = 4 * (256 / n_eq);
-    if (tb > 256) tb = 256;
-    a.TB = tb;
+    const int n_tq = 256 / n_eq;
+    // largest micro-tile height that still gives every CU a workgroup
+    int mr = 4;
+    while (mr > 1 && (T + (int64_t)std::min(256, mr * n_tq) - 1) / std::min(256, mr * n_tq) < cus) mr >>= 1;
+    a.MR = mr;
+    a.TB = std::min(256 / mr, n_tq) * mr;
     int g = 1;
     while (g < E && g < kWave) g <<= 1;
     a.G = g;
+    const int vec = dtype == MOE_BF16 ? 8 : 4;
     const int budget = 16384;  // floats of LDS per workgroup (64 KiB)
     int kc = 64;
-    while (kc > 4 && a.TB * (kc + 1) + kc * a.Epad + a.TB * (a.Epad + 1) > budget) kc >>= 1;
+    while (kc > 8 && (a.TB * kc / vec > 256 * kMaxXV || kc * EP2 > 256 * kMaxWS ||
+                      a.TB * (kc + 1) + 3 + kc * EP2 + a.TB * (a.Epad + 1) > budget))
+        kc >>= 1;
     a.KC = kc;
+    a.lkv = ilog2(kc / vec);
     return a;
 }
 
 size_t route_smem_bytes(const RouteArgs& a) {
-    return sizeof(float) * ((size_t)a.TB * (a.KC + 1) + (size_t)a.KC * a.Epad +
+    return sizeof(float) * ((((size_t)a.TB * (a.KC + 1) + 3) & ~size_t(3)) + ((size_t)a.KC << a.lep) +
                             (size_t)a.TB * (a.Epad + 1));
+}
+
+template <typename XT, int MR>
+static void launch_gate_mr(const RouteArgs& a, dim3 grid, size_t sm, hipStream_t st) {
+    switch (route_nv(a.E, a.G)) {
+        case 1: hipLaunchKernelGGL((route_gate_topk_kernel<XT, MR, 1>), grid, dim3(256), sm, st, a); break;
+        case 2: hipLaunchKernelGGL((route_gate_topk_kernel<XT, MR, 2>), grid, dim3(256), sm, st, a); break;
+        case 4: hipLaunchKernelGGL((route_gate_topk_kernel<XT, MR, 4>), grid, dim3(256), sm, st, a); break;
+        case 8: hipLaunchKernelGGL((route_gate_topk_kernel<XT, MR, 8>), grid, dim3(256), sm, st, a); break;
+        default: hipLaunchKernelGGL((route_gate_topk_kernel<XT, MR, 16>), grid, dim3(256), sm, st, a); break;
+    }
 }
 
 template <typename XT>
 static hipError_t launch_gate_t(const RouteArgs& a, hipStream_t st) {
-    const dim3 grid((unsigned)((a.T + a.TB - 1) / a.TB)), block(256);
+    const dim3 grid((unsigned)((a.T + a.TB - 1) / a.TB));
     const size_t sm = route_smem_bytes(a);
-    switch (route_nv(a.E, a.G)) {
-        case 1: hipLaunchKernelGGL((route_gate_topk_kernel<XT, 1>), grid, block, sm, st, a); break;
-        case 2: hipLaunchKernelGGL((route_gate_topk_kernel<XT, 2>), grid, block, sm, st, a); break;
-        case 4: hipLaunchKernelGGL((route_gate_topk_kernel<XT, 4>), grid, block, sm, st, a); break;
-        case 8: hipLaunchKernelGGL((route_gate_topk_kernel<XT, 8>), grid, block, sm, st, a); break;
-        default: hipLaunchKernelGGL((route_gate_topk_kernel<XT, 16>), grid, block, sm, st, a); break;
-    }
+    if (a.MR == 4) launch_gate_mr<XT, 4>(a, grid, sm, st);
+    else if (a.MR == 2) launch_gate_mr<XT, 2>(a, grid, sm, st);
+    else launch_gate_mr<XT, 1>(a, grid, sm, st);
     return hipGetLastError();
 }
 

@@ -65,10 +65,11 @@ def test_capacity_agrees_with_oracle(moe, orc):
 def test_workspace_layout(moe):
     s = moe.shape(8192, 2048, 64, 2, 8192, 2.0)
     n = moe.moe_workspace_size(s)
-    offs = [moe.moe_workspace_offset(s, w) for w in range(5)]
+    offs = [moe.moe_workspace_offset(s, w) for w in range(6)]
     assert all(o % 256 == 0 for o in offs)
     assert offs[moe.MOE_WS_H] + 16384 * 8192 * 2 <= n
     assert offs[moe.MOE_WS_XPERM] + 16384 * 2048 * 2 <= offs[moe.MOE_WS_H]
+    assert offs[moe.MOE_WS_OUT] + 16384 * 2048 * 4 <= n
     assert moe.moe_workspace_offset(s, 99) == -1
 
 
@@ -119,9 +120,9 @@ def test_null_misaligned_and_workspace_errors(moe):
 
 
 def test_stage_hook_validation(moe):
-    assert moe.moe_stage_names() == ["route", "hist", "scatter", "gather", "ffn1", "ffn2_combine"]
+    assert moe.moe_stage_names() == ["route", "hist", "scatter", "gather", "ffn1", "ffn2", "combine"]
     with pytest.raises(moe.MoEError):
-        moe._check(moe._lib.moe_set_stage_events(None, 12))
+        moe._check(moe._lib.moe_set_stage_events(None, 14))
     arr = (C.c_void_p * 3)()
     with pytest.raises(moe.MoEError):
         moe._check(moe._lib.moe_set_stage_events(arr, 3))
