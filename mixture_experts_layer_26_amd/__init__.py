@@ -56,7 +56,7 @@ _sigs = {
     "moe_num_stages": (C.c_int, []),
     "moe_stage_name": (C.c_char_p, [C.c_int]),
     "moe_set_stage_events": (C.c_int, [C.POINTER(_P), C.c_int]),
-    "moe_route": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_route": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "moe_route_logits": (C.c_int, [_SP, _P, _P, _P, _P]),
     "moe_dispatch": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "moe_grouped_ffn": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
@@ -132,9 +132,13 @@ def moe_set_stage_events(events: Sequence) -> None:
     _check(_lib.moe_set_stage_events(arr, len(events)))
 
 
-def moe_route(s, x, Wg, bg, logits, topk_idx, topk_w, stream=None) -> None:
+def _ws_bytes(ws) -> int:
+    return 0 if ws is None or isinstance(ws, int) else ws.numel() * ws.element_size()
+
+
+def moe_route(s, x, Wg, bg, logits, topk_idx, topk_w, ws, stream=None) -> None:
     _check(_lib.moe_route(C.byref(s), _ptr(x), _ptr(Wg), _ptr(bg), _ptr(logits), _ptr(topk_idx),
-                          _ptr(topk_w), _stream(stream)))
+                          _ptr(topk_w), _ptr(ws), _ws_bytes(ws), _stream(stream)))
 
 
 def moe_route_logits(s, logits, topk_idx, topk_w, stream=None) -> None:

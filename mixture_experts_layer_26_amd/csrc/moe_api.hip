@@ -49,6 +49,7 @@ struct Geo {
     int64_t T, d, E, k, dff, cap, max_rows;
     int esz;      // bytes per element of x / W / h
     int BT, nblk; // dispatch token blocks
+    bool mfma_gate; // gate on matrix cores (bf16 x, E <= 256)
 };
 
 // cap = min(T, ceil(cf * T * k / E)); cf <= 0: no limit.  cf*T*k is exact in
@@ -92,12 +93,13 @@ static int validate(const moe_shape* s, Geo* g) {
         g->esz = s->dtype == MOE_BF16 ? 2 : 4;
         g->BT = dispatch_block_tokens((int)s->E);
         g->nblk = (int)((s->T + g->BT - 1) / g->BT);
+        g->mfma_gate = route_mfma_supported(s->dtype, (int)s->E, (int)s->k);
     }
     return MOE_OK;
 }
 
 struct WsLayout {
-    size_t blkhist, offsets, idx, w, perm, slot, xperm, h, out, total;
+    size_t gate, blkhist, offsets, idx, w, perm, slot, xperm, h, out, total;
 };
 
 static size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
@@ -110,6 +112,7 @@ static WsLayout ws_layout(const Geo& g) {
         p = align_up(p + (bytes ? bytes : 1));
         return at;
     };
+    L.gate = take(g.mfma_gate ? route_mfma_ws_bytes((int)g.d, (int)g.E) : 0);
     L.blkhist = take(sizeof(int32_t) * (size_t)g.nblk * g.E);
     L.offsets = take(sizeof(int32_t) * (size_t)(g.E + 1));
     L.idx = take(sizeof(int32_t) * (size_t)(g.T * g.k));
@@ -161,6 +164,12 @@ static void stage_event(int stage, int after, hipStream_t st) {
     if (!g_events_armed) return;
     const size_t i = 2 * (size_t)stage + after;
     if (i < g_events.size() && g_events[i] != nullptr) (void)hipEventRecord(g_events[i], st);
+}
+
+static hipError_t launch_route(const Geo& g, const moe_shape* s, const RouteArgs& ra, void* ws,
+                               const WsLayout& L, hipStream_t st) {
+    if (g.mfma_gate) return launch_route_mfma(ra, at<uint16_t>(ws, L.gate), device_cu_count(), st);
+    return launch_route_gate(ra, s->dtype, st);
 }
 
 static DispatchArgs dispatch_args(const Geo& g, const moe_shape* s) {
@@ -251,7 +260,7 @@ int moe_set_stage_events(void** events, int n_events) {
 }
 
 int moe_route(const moe_shape* s, const void* x, const float* Wg, const float* bg, float* logits,
-              int32_t* topk_idx, float* topk_w, void* stream) {
+              int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes, void* stream) {
     Geo g;
     if (int rc = validate(s, &g)) return rc;
     MOE_REQUIRE(x);
@@ -260,6 +269,8 @@ int moe_route(const moe_shape* s, const void* x, const float* Wg, const float* b
     MOE_OPTIONAL(logits);
     MOE_REQUIRE(topk_idx);
     MOE_REQUIRE(topk_w);
+    WsLayout L;
+    if (int rc = check_ws(g, ws, ws_bytes, &L)) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
     RouteArgs a = route_config(g.T, (int)g.d, (int)g.E, (int)g.k, s->temperature, s->dtype, device_cu_count());
     a.x = x;
@@ -268,7 +279,7 @@ int moe_route(const moe_shape* s, const void* x, const float* Wg, const float* b
     a.logits = logits;
     a.idx = topk_idx;
     a.w = topk_w;
-    MOE_HIP(launch_route_gate(a, s->dtype, st), "route kernel launch");
+    MOE_HIP(launch_route(g, s, a, ws, L, st), "route kernel launch");
     return MOE_OK;
 }
 
@@ -417,7 +428,7 @@ int moe_layer_forward(const moe_shape* s, const void* x, const float* Wg, const 
     ra.idx = idx;
     ra.w = w;
     stage_event(0, 0, st);
-    MOE_HIP(launch_route_gate(ra, s->dtype, st), "route kernel launch");
+    MOE_HIP(launch_route(g, s, ra, ws, L, st), "route kernel launch");
     stage_event(0, 1, st);
 
     // 2. dispatch

@@ -25,6 +25,11 @@ size_t route_smem_bytes(const RouteArgs& a);
 hipError_t launch_route_gate(const RouteArgs& a, int dtype, hipStream_t st);
 hipError_t launch_route_logits(const RouteArgs& a, hipStream_t st);
 
+// ---- route_mfma.hip (bf16 x, E <= 256): fp32-accurate gate on MFMA ------
+bool route_mfma_supported(int dtype, int E, int k);
+size_t route_mfma_ws_bytes(int d, int E);   // the three bf16 parts of Wg
+hipError_t launch_route_mfma(const RouteArgs& a, uint16_t* W3, int cus, hipStream_t st);
+
 // ---- dispatch.hip -------------------------------------------------------
 struct DispatchArgs {
     int64_t T;

@@ -90,7 +90,7 @@ def test_invalid_shapes_rejected_before_launch(moe, bad):
     assert moe.moe_capacity(s) == -1
     p = 0x10000  # never dereferenced: validation fails first
     with pytest.raises(moe.MoEError) as ei:
-        moe.moe_route(s, p, p, None, None, p, p, stream=0)
+        moe.moe_route(s, p, p, None, None, p, p, p, stream=0)
     assert ei.value.status == 2
     with pytest.raises(moe.MoEError) as ei:
         moe._check(moe._lib.moe_layer_forward(C.byref(s), p, p, None, p, p, p, p, p, p, p,
@@ -102,11 +102,14 @@ def test_null_misaligned_and_workspace_errors(moe):
     s = moe.shape(64, 64, 8, 2, 128, 1.0)
     p = 0x10000
     with pytest.raises(moe.MoEError) as ei:
-        moe.moe_route(s, None, p, None, None, p, p, stream=0)
+        moe.moe_route(s, None, p, None, None, p, p, p, stream=0)
     assert ei.value.status == 1 and "x is NULL" in str(ei.value)
     with pytest.raises(moe.MoEError) as ei:
-        moe.moe_route(s, p + 4, p, None, None, p, p, stream=0)
+        moe.moe_route(s, p + 4, p, None, None, p, p, p, stream=0)
     assert ei.value.status == 4
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_route(s, p, p, None, None, p, p, None, stream=0)
+    assert ei.value.status == 5
     need = moe.moe_workspace_size(s)
     with pytest.raises(moe.MoEError) as ei:
         moe._check(moe._lib.moe_dispatch(C.byref(s), p, p, None, p, p, p, p, p, p, need - 1, None))

@@ -95,7 +95,7 @@ def _check_case(moe, orc, name):
     idx2 = H.empty((T, k), i32)
     w2 = H.empty((T, k), f32)
     logits2 = H.empty((T, E), f32)
-    moe.moe_route(s, dv["x"], dv["Wg"], dv["bg"], logits2, idx2, w2)
+    moe.moe_route(s, dv["x"], dv["Wg"], dv["bg"], logits2, idx2, w2, ws)
     counts2 = H.empty(E, i32)
     routed2 = H.empty(E, i32)
     offsets2 = H.empty(E + 1, i32)
