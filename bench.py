@@ -31,16 +31,27 @@ METRIC = "MoE layer fwd tokens/sec + grouped-GEMM % peak MFMA, E=64 top-2 d=2048
 PEAK_HBM = 8.0e12          # B/s, MI355X HBM3E
 PEAK_BF16 = 2.5e15         # FLOP/s, dense bf16 matrix
 PEAK_FP32 = 157.3e12       # FLOP/s, fp32
-GEMM_SOURCES = ["mixture_experts_layer_26_amd/csrc/ffn_bf16.hip",
-                "mixture_experts_layer_26_amd/csrc/ffn_sched.h",
-                "mixture_experts_layer_26_amd/csrc/moe_common.h"]
+CSRC = os.path.join(ROOT, "mixture_experts_layer_26_amd", "csrc")
+COPY_CALIB_BYTES = 1 << 30
+# kernel-name patterns of the launches each stage makes (bf16 path)
+STAGE_KERNELS = {
+    "route": ("route_mfma_kernel", "gate_topk_kernel"),
+    "hist": ("hist_kernel",),
+    "scatter": ("scatter_kernel",),
+    "gather": ("gather_kernel",),
+    "ffn1": ("ffn_gemm_bf16_kernel<", ", 0>"),
+    "ffn2": ("ffn_gemm_bf16_kernel<", ", 1>"),
+    "combine": ("combine_kernel",),
+}
 
 
 def kernel_source_hash() -> str:
+    """Hash of every kernel source: counter records taken from other sources
+    no longer describe the kernels that run."""
     h = hashlib.sha256()
-    for p in GEMM_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
@@ -55,6 +66,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic_<stage>_<workload>.json from the "
+                         "counter_collection.csv of a FETCH_SIZE and a WRITE_SIZE "
+                         "rocprofv3 --pmc run of this script with --copy-calib")
     return ap.parse_args()
 
 
@@ -63,7 +78,7 @@ def stage_bytes_flops(cfg, S, active, esz, nblk):
     or compute over the kept slots; no dense T x E work)."""
     T, d, E, k, F = cfg.T, cfg.d, cfg.E, cfg.k, cfg.d_ff
     return {
-        "route": (T * d * esz + d * E * 4 + T * k * 8 + T * d * 4, 2 * T * d * E),
+        "route": (T * d * esz + d * E * 4 + T * k * 8, 2 * T * d * E),
         "hist": (T * k * 4 + nblk * E * 4, 0),
         "scatter": (nblk * nblk * E * 4 + T * k * 12 + S * 8, 0),
         "gather": (2 * S * d * esz, 0),
@@ -107,6 +122,67 @@ def cpu_baseline(cfg, inp, budget_s):
     }
 
 
+def _stage_of(kernel: str):
+    for stage, pats in STAGE_KERNELS.items():
+        if stage.startswith("ffn"):
+            if all(p in kernel for p in pats):
+                return stage
+        elif any(p in kernel for p in pats):
+            return stage
+    return None
+
+
+def write_traffic(fetch_csv: str, write_csv: str, workload: str, steps: int) -> None:
+    """HBM bytes per launch of each stage from the FETCH_SIZE / WRITE_SIZE
+    counters (KiB per dispatch).  Each counter is scaled by what it reads for
+    the plain copy of COPY_CALIB_BYTES that --copy-calib runs; the last
+    `steps` dispatches of each kernel (the timed ones) are averaged."""
+    import csv
+    import numpy as np
+
+    def per_kernel(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        by = {}
+        for r in rows:
+            by.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return by
+
+    fe, wr = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    kib = COPY_CALIB_BYTES / 1024
+
+    def calib(by):
+        vals = [v for name, vs in by.items() if "copyBuffer" in name for v in vs]
+        big = max(vals)
+        return kib / float(np.mean([v for v in vals if v > 0.5 * big]))
+
+    f_fetch, f_write = calib(fe), calib(wr)
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    for name in fe:
+        stage = _stage_of(name)
+        if stage is None or name not in wr:
+            continue
+        fk = float(np.mean(fe[name][-steps:]))
+        wk = float(np.mean(wr[name][-steps:]))
+        rec = {
+            "workload": workload, "stage": stage, "kernel": name,
+            "bytes_per_launch": (fk * f_fetch + wk * f_write) * 1024,
+            "fetch_bytes": fk * f_fetch * 1024, "write_bytes": wk * f_write * 1024,
+            "fetch_kib_raw": fk, "write_kib_raw": wk,
+            "calib_fetch_factor": f_fetch, "calib_write_factor": f_write,
+            "dispatches_averaged": min(steps, len(fe[name])),
+            "kernel_source_hash": kernel_source_hash(),
+            "commands": [
+                f"rocprofv3 --pmc {c} --output-format csv -d <dir> -o run -- python3 bench.py "
+                f"--config {workload} --steps {steps} --warmup 1 --no-cpu-baseline --copy-calib"
+                for c in ("FETCH_SIZE", "WRITE_SIZE")],
+        }
+        with open(os.path.join(ROOT, "profiles", f"traffic_{stage}_{workload}.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+        print(f"{stage:8s} {rec['bytes_per_launch'] / 1e9:8.4f} GB/launch  "
+              f"(fetch x{f_fetch:.3f}, write x{f_write:.3f})")
+
+
 def load_traffic(workload: str, stage: str):
     p = os.path.join(ROOT, "profiles", f"traffic_{stage}_{workload}.json")
     if not os.path.exists(p):
@@ -120,6 +196,10 @@ def load_traffic(workload: str, stage: str):
 
 def main():
     args = parse()
+    if args.traffic_from:
+        from moe_inputs import HEADLINE
+        write_traffic(*args.traffic_from, args.config or HEADLINE, args.steps)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}), flush=True)
@@ -238,12 +318,12 @@ def main():
         "setup_seconds": round(t_gen, 2),
     }
     if args.copy_calib:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        src = torch.empty(COPY_CALIB_BYTES, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
-        out["copy_calib_bytes"] = 1 << 30
+        out["copy_calib_bytes"] = COPY_CALIB_BYTES
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
     print(json.dumps(out), flush=True)
