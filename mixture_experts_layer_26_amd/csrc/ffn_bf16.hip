@@ -11,25 +11,29 @@
 //
 // Work list: persistent workgroups walk (expert, n-tile, m-tile) items, see
 // ffn_sched.h.  Per item a BM x BN output tile accumulates over K in steps
-// of 32 through an NSTAGE-deep ring of LDS buffers:
+// of 32 through a ring of NSTAGE LDS slots:
 //   * operands go global -> LDS with buffer_load_dwordx4 ... lds (no VGPR
 //     staging); each wave instruction fills 1 KiB of LDS, lane L the L-th
 //     16 bytes.  The buffer descriptor's range ends at the expert's last row
 //     (activations) or matrix end (weights), so rows past the segment and
 //     the K tail read as zeros; the column tail is steered out of range.
-//   * loads run NSTAGE-1 steps ahead; one s_waitcnt vmcnt + s_barrier per
-//     step publishes the oldest stage and frees the one consumed before it;
-//     the next item's first stages are issued before the current item's
-//     epilogue, so its arithmetic and stores overlap those loads.
+//   * the weight is the MFMA A operand and the token rows the B operand, so
+//     each lane's accumulator holds runs of four consecutive output columns
+//     of one row.  Activation rows are K-contiguous (16-byte ds_read_b128);
+//     weights are N-contiguous and are transposed on the way out of LDS by
+//     ds_read_b64_tr_b16.  Both LDS tiles are XOR-swizzled at 16-byte
+//     granularity so the lanes served together fall on distinct banks.
 //   * GEMM1's epilogue is bias + GELU (Abramowitz & Stegun 7.1.26 erf, error
 //     below 1.5e-7, well under the bf16 rounding of h) + bf16 rounding.
-//   * v_mfma_f32_16x16x32_bf16 with the weight as the A operand and the
-//     token rows as the B operand, so each lane's accumulator holds four
-//     consecutive output columns of one row.  Activation rows are
-//     K-contiguous (16-byte ds_read_b128); weights are N-contiguous and are
-//     transposed on the way out of LDS by ds_read_b64_tr_b16.
-//   * both LDS tiles are XOR-swizzled at 16-byte granularity so the reads of
-//     a 16-lane group fall on distinct banks.
+//
+// Two schedules:
+//   * large problems: 256 x 256 tiles on eight waves (two per SIMD), each a
+//     128 x 64 quarter-column of the tile on v_mfma_f32_32x32x16_bf16 (one
+//     wave issues these back to back; the 16x16x32 form with accumulators in
+//     VGPRs cannot).  Every wave reads the next step's fragments into a second
+//     register set while its MFMAs run, and the ring continues across items.
+//   * small problems: 128 x 128 tiles, four waves on v_mfma_f32_16x16x32_bf16,
+//     one barrier per step (read, then multiply).
 #include "ffn_sched.h"
 #include "moe_kernels.h"
 
@@ -40,43 +44,44 @@ namespace {
 constexpr int BK = 32;      // K per pipeline stage
 constexpr int NSTAGE = 4;   // LDS ring depth
 
-template <int BM_, int BN_, int WM_, int WN_>
+// MF: 16 (v_mfma_f32_16x16x32_bf16) or 32 (v_mfma_f32_32x32x16_bf16)
+template <int BM_, int BN_, int WM_, int WN_, int MF_>
 struct TileCfg {
-    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, MF = MF_;
     static constexpr int NT = 64 * WM * WN;          // threads
     static constexpr int NW = WM * WN;               // waves
     static constexpr int TM = BM / WM, TN = BN / WN; // wave tile
-    static constexpr int MB = TM / 16, NB = TN / 16; // 16x16 blocks per wave
+    static constexpr int MB = TM / MF, NB = TN / MF; // MFMA blocks per wave
     static constexpr int A_BYTES = BM * BK * 2;      // one stage of activations
     static constexpr int B_BYTES = BK * BN * 2;      // one stage of weights
     static constexpr int A_DMA = A_BYTES / 1024 / NW;  // 1 KiB wave loads per wave per stage
     static constexpr int B_DMA = B_BYTES / 1024 / NW;
     static constexpr int B_ROW_CHUNKS = BN / 8;      // 16-byte chunks per weight row
-    static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be a multiple of 16");
+    static_assert(MF == 16 || MF == 32, "MFMA shape");
+    static_assert(TM % MF == 0 && TN % MF == 0, "wave tile must be a multiple of the MFMA block");
     static_assert(A_DMA * 1024 * NW == A_BYTES && B_DMA * 1024 * NW == B_BYTES, "stage must split into wave loads");
     static_assert(B_ROW_CHUNKS >= 16 && 64 % B_ROW_CHUNKS == 0, "weight row layout (BN 128 or 256)");
 };
 
-// Two tile shapes: the large one when the work list still gives every CU a
-// few items, the small one otherwise (launch_ffn_gemm_bf16).
-#ifndef MOE_TILE_LARGE
-#define MOE_TILE_LARGE 256, 256, 2, 4
-#endif
 #ifndef MOE_TILE_SMALL
-#define MOE_TILE_SMALL 128, 128, 2, 2
+#define MOE_TILE_SMALL 128, 128, 2, 2, 16
 #endif
-using TileLarge = TileCfg<MOE_TILE_LARGE>;
+#ifndef MOE_TILE_PIPE
+#define MOE_TILE_PIPE 256, 256, 2, 4, 32
+#endif
 using TileSmall = TileCfg<MOE_TILE_SMALL>;
+using TilePipe = TileCfg<MOE_TILE_PIPE>;
 
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 // 16 bytes per lane, global -> LDS at (lds + 16 * lane).  Issued as inline asm
 // so that the compiler's wait insertion neither tracks it nor adds vmcnt
-// waits for it: every wait on these loads is explicit (wait_vm_barrier).
+// waits for it: every wait on these loads is explicit.
 __device__ __forceinline__ void dma16(const i32x4_t& rsrc, const void* lds, int voffset) {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds));
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :: "s"(m0), "v"(voffset), "s"(rsrc) : "memory");
+                 :: "s"(m0), "v"(voffset), "s"(rsrc) : "memory", "m0");
 }
 
 // Buffer descriptor: 48-bit base, stride 0, range in bytes, gfx9 data format.
@@ -101,16 +106,28 @@ __device__ __forceinline__ bf16x8_t cat8(bf16x4_t lo, bf16x4_t hi) {
 }
 
 // Activation tile, one stage: row r (BM rows) holds K 0..31 as four 16-byte
-// chunks; logical chunk c sits at physical slot c ^ ((r >> 1) & 3), which
-// spreads the 16 rows read by one 16-lane group over all banks.
-__device__ __forceinline__ int a_swz(int r) { return (r >> 1) & 3; }
-__device__ __forceinline__ int a_slot(int r, int c) { return r * 4 + (c ^ a_swz(r)); }
+// chunks; logical chunk c sits at physical slot c ^ a_swz<MF>(r), which puts
+// the rows read together by one fragment read on distinct banks (both
+// choices measured conflict-free with SQ_LDS_BANK_CONFLICT on MI355X).
+template <int MF>
+__device__ __forceinline__ int a_swz(int r) { return MF == 16 ? (r >> 1) & 3 : (r >> 2) & 3; }
+template <int MF>
+__device__ __forceinline__ int a_slot(int r, int c) { return r * 4 + (c ^ a_swz<MF>(r)); }
+
 // Weight tile, one stage: row k (32 rows) holds BN columns as BN/8 chunks;
-// logical chunk c sits at physical chunk c ^ (2 (k & 3)) ^ (8 ((k >> 3) & 1)):
-// a 16-lane transposed read covers rows k..k+3 and two adjacent chunks, and
-// the two 16-lane groups served together read rows 8 apart.
-__device__ __forceinline__ int b_swz(int k) { return (2 * (k & 3)) ^ (8 * ((k >> 3) & 1)); }
-__device__ __forceinline__ int b_chunk(int k, int c) { return c ^ b_swz(k); }
+// logical chunk c sits at physical chunk c ^ b_swz<MF>(k).  A 16-lane
+// transposed read covers rows k..k+3 and two adjacent chunks.
+//   MF 16: the two 16-lane groups served together read rows 8 apart:
+//          c ^ (2 (k & 3)) ^ (8 ((k >> 3) & 1)).
+//   MF 32: they read the same rows and the next two chunks: c ^ (4 (k & 3)),
+//          so the four rows of a 4-chunk window land on distinct banks.
+// (both measured conflict-free with SQ_LDS_BANK_CONFLICT on MI355X)
+template <int MF>
+__device__ __forceinline__ int b_swz(int k) {
+    return MF == 16 ? (2 * (k & 3)) ^ (8 * ((k >> 3) & 1)) : 4 * (k & 3);
+}
+template <int MF>
+__device__ __forceinline__ int b_chunk(int k, int c) { return c ^ b_swz<MF>(k); }
 
 // wait until at most n vector-memory operations of this wave are in flight,
 // then meet the other waves of the workgroup
@@ -121,88 +138,302 @@ __device__ __forceinline__ void wait_vm_barrier() {
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-}  // namespace
+// s_waitcnt immediate (gfx9 layout: vmcnt in bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8); expcnt is never waited on here
+constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
 
-template <class C, int EPI>
-__global__ __launch_bounds__(C::NT) void ffn_gemm_bf16_kernel(GemmArgs g) {
-    __shared__ __attribute__((aligned(1024))) uint16_t sa[NSTAGE][C::BM * BK];
-    __shared__ __attribute__((aligned(1024))) uint16_t sb[NSTAGE][BK * C::BN];
-    __shared__ int mt_pre[1025];
-    __shared__ int scan_tmp[32];
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wid = tid / kWave;
-    const int wm = wid / C::WN, wn = wid % C::WN;
-    const int g16 = lane >> 4, i16 = lane & 15;
-    const int E = g.E, K = g.K, N = g.N;
-    const int ntn = (N + C::BN - 1) / C::BN;
-    const int nk = (K + BK - 1) / BK;
+// vmcnt(VM) lgkmcnt(0) then the workgroup barrier.  The wait goes through the
+// builtin so the compiler's own wait insertion knows every LDS read has
+// returned; the barrier is asm with a memory clobber so no LDS access moves
+// across it, and the scheduling barriers keep the MFMAs of a step inside it.
+template <int VM>
+__device__ __forceinline__ void pipe_barrier() {
+    static_assert(VM >= 0 && VM < 64, "vmcnt range");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(VM, 0));
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
 
-    const int total_mt = build_mtile_prefix(g.offsets, E, C::BM, mt_pre, scan_tmp);
-    const ItemRange range = xcd_item_range((int64_t)total_mt * ntn);
-    if (range.first >= range.end) return;
+// fp32 pair -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    const f2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2));
+}
 
-    const uint16_t* __restrict__ A = static_cast<const uint16_t*>(g.A);
-    const uint16_t* __restrict__ Bw = static_cast<const uint16_t*>(g.B);
+// bias + activation + store of four consecutive columns of one row
+template <int EPI>
+__device__ __forceinline__ void store4(const GemmArgs& g, int64_t row, int n, f32x4_t v) {
+    if constexpr (EPI == EPI_GELU_H) {
+        uint2 pk;
+        pk.x = pack_bf16x2(gelu_as(v[0]), gelu_as(v[1]));
+        pk.y = pack_bf16x2(gelu_as(v[2]), gelu_as(v[3]));
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(g.out) + row * g.N + n) = pk;
+    } else {
+        *reinterpret_cast<f32x4_t*>(static_cast<float*>(g.out) + row * g.N + n) = v;
+    }
+}
 
-    // DMA geometry of this lane (independent of the item):
-    //   A: wave instruction covers 16 rows; lane -> (row, physical slot)
-    const int a_rl = lane >> 2, a_ps = lane & 3;
-    //   B: wave instruction covers 512 / BN rows; lane -> (row, physical chunk)
-    constexpr int B_ROWS_PER_DMA = 512 / C::BN;
-    const int b_rl = lane / C::B_ROW_CHUNKS, b_pc = lane % C::B_ROW_CHUNKS;
+// Per-lane global -> LDS load geometry and the work item it streams from.
+template <class C>
+struct Item {
+    int e, m0, mrows, n0;
+    i32x4_t rsA, rsB;
+    int a_off[C::A_DMA], b_off[C::B_DMA];
+};
 
-    struct Item {
-        int e, m0, mrows, n0;
-        i32x4_t rsA, rsB;
-        int a_off[C::A_DMA], b_off[C::B_DMA];
-    };
-    auto setup = [&](int64_t item, Item& it) {
+template <class C>
+struct Loader {
+    const uint16_t* A;
+    const uint16_t* Bw;
+    const int* s_off;    // expert row offsets, copied to LDS
+    const int* mt_pre;   // m-tile prefix, LDS
+    int E, K, N, ntn, wid;
+    int a_rl, a_ps, b_rl, b_pc;
+    static constexpr int B_ROWS_PER_DMA = 512 / C::BN;
+
+    __device__ __forceinline__ Loader(const GemmArgs& g, const int* off, const int* pre, int ntn_, int wid_,
+                                      int lane)
+        : A(static_cast<const uint16_t*>(g.A)), Bw(static_cast<const uint16_t*>(g.B)), s_off(off),
+          mt_pre(pre), E(g.E), K(g.K), N(g.N), ntn(ntn_), wid(wid_) {
+        // A: a wave instruction covers 16 rows; lane -> (row, physical slot)
+        a_rl = lane >> 2;
+        a_ps = lane & 3;
+        // B: a wave instruction covers 512 / BN k-rows; lane -> (k-row, physical chunk)
+        b_rl = lane / C::B_ROW_CHUNKS;
+        b_pc = lane % C::B_ROW_CHUNKS;
+    }
+
+    // expert, first row, row count and first column of an item (LDS reads only)
+    __device__ __forceinline__ void decode(int64_t item, Item<C>& it) const {
         const WorkItem wi = decode_item(mt_pre, E, ntn, item);
-        it.e = wi.e;
-        it.m0 = g.offsets[wi.e] + wi.mt * C::BM;
-        it.mrows = min(C::BM, g.offsets[wi.e + 1] - it.m0);
-        it.n0 = wi.nt * C::BN;
+        const int e = __builtin_amdgcn_readfirstlane(wi.e);
+        const int m0 = __builtin_amdgcn_readfirstlane(s_off[e] + wi.mt * C::BM);
+        it.e = e;
+        it.m0 = m0;
+        it.mrows = __builtin_amdgcn_readfirstlane(min(C::BM, s_off[e + 1] - m0));
+        it.n0 = __builtin_amdgcn_readfirstlane(wi.nt * C::BN);
+    }
+
+    __device__ __forceinline__ void setup(int64_t item, Item<C>& it) const {
+        decode(item, it);
         // activations: the range ends at the expert's last row, so rows past the
         // segment read zeros; a K tail reads the next row's head, which meets the
         // zero weight rows past K (finite inputs)
         it.rsA = make_rsrc(A + (int64_t)it.m0 * K, (uint32_t)it.mrows * (uint32_t)K * 2u);
-        it.rsB = make_rsrc(Bw + (int64_t)wi.e * K * N, (uint32_t)K * (uint32_t)N * 2u);
+        it.rsB = make_rsrc(Bw + (int64_t)it.e * K * N, (uint32_t)K * (uint32_t)N * 2u);
 #pragma unroll
         for (int j = 0; j < C::A_DMA; ++j) {
             const int r = (wid * C::A_DMA + j) * 16 + a_rl;   // tile row
-            const int c = a_ps ^ a_swz(r);                      // logical chunk
+            const int c = a_ps ^ a_swz<C::MF>(r);               // logical chunk
             it.a_off[j] = (r * K + c * 8) * 2;
         }
 #pragma unroll
         for (int j = 0; j < C::B_DMA; ++j) {
             const int k = (wid * C::B_DMA + j) * B_ROWS_PER_DMA + b_rl;   // tile k-row
-            const int c = b_pc ^ b_swz(k);                                  // logical chunk
+            const int c = b_pc ^ b_swz<C::MF>(k);                           // logical chunk
             const int col = it.n0 + c * 8;
             it.b_off[j] = (col < N) ? (k * N + col) * 2 : kOutOfRange;
         }
-    };
-    auto issue = [&](const Item& it, int kt) {
-        const int buf = kt % NSTAGE;
+    }
+
+    // PER = A_DMA + B_DMA loads of K-step kt of `it` into one ring slot
+    __device__ __forceinline__ void issue(const Item<C>& it, int kt, uint16_t* sa_buf, uint16_t* sb_buf) const {
         const int k0 = kt * BK;
 #pragma unroll
         for (int j = 0; j < C::A_DMA; ++j)
-            dma16(it.rsA, &sa[buf][(wid * C::A_DMA + j) * 512], it.a_off[j] + k0 * 2);
+            dma16(it.rsA, sa_buf + (wid * C::A_DMA + j) * 512, it.a_off[j] + k0 * 2);
 #pragma unroll
         for (int j = 0; j < C::B_DMA; ++j) {
             const int off = (it.b_off[j] == kOutOfRange) ? kOutOfRange : it.b_off[j] + k0 * N * 2;
-            dma16(it.rsB, &sb[buf][(wid * C::B_DMA + j) * 512], off);
+            dma16(it.rsB, sb_buf + (wid * C::B_DMA + j) * 512, off);
         }
-    };
-    auto prologue = [&](const Item& it) {
-        for (int s = 0; s < NSTAGE - 1 && s < nk; ++s) issue(it, s);
-    };
+    }
+
+    // the item's BN bias values (fp32, 1 KiB) into LDS: one wave instruction,
+    // columns past N read zeros
+    __device__ __forceinline__ void issue_bias(const Item<C>& it, const float* bias, int lane, float* dst) const {
+        static_assert(C::BN == 256, "one wave instruction per bias slice");
+        const i32x4_t rs = make_rsrc(bias + (int64_t)it.e * N, (uint32_t)N * 4u);
+        dma16(rs, dst, (it.n0 + 4 * lane) * 4);
+    }
+
+    // the same number of loads, all out of range: they fill the slot with
+    // zeros and touch no memory (keeps every wave's load count per step fixed)
+    __device__ __forceinline__ void issue_zero(const Item<C>& it, uint16_t* sa_buf, uint16_t* sb_buf) const {
+#pragma unroll
+        for (int j = 0; j < C::A_DMA; ++j) dma16(it.rsA, sa_buf + (wid * C::A_DMA + j) * 512, kOutOfRange);
+#pragma unroll
+        for (int j = 0; j < C::B_DMA; ++j) dma16(it.rsB, sb_buf + (wid * C::B_DMA + j) * 512, kOutOfRange);
+    }
+};
+
+// ---- 16x16x32 fragments (small tiles) ------------------------------------
+// One K-step of a wave tile: NB weight fragments (transposed out of LDS) and
+// MB activation fragments; lane l holds row / column l % 16, K 8 (l / 16)..+7.
+template <class C>
+struct Frags16 {
+    bf16x8_t w[C::NB];
+    bf16x8_t t[C::MB];
+};
+
+template <class C>
+__device__ __forceinline__ void read_frags16(Frags16<C>& f, const uint16_t* as, const uint16_t* bs, int wm, int wn,
+                                             int lane) {
+    const int g16 = lane >> 4, i16 = lane & 15;
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb) {
+        // rows 8 g16 + (i16 >> 2) (+4), columns 4 (i16 & 3) of the 16-column block
+        const int col = wn * C::TN + nb * 16 + 4 * (i16 & 3);
+        const int k = 8 * g16 + (i16 >> 2);
+        const int c = col >> 3, half = (col & 7);
+        const bf16x4_t lo = lds_read_tr(&bs[k * C::BN + b_chunk<16>(k, c) * 8 + half]);
+        const bf16x4_t hi = lds_read_tr(&bs[(k + 4) * C::BN + b_chunk<16>(k + 4, c) * 8 + half]);
+        f.w[nb] = cat8(lo, hi);
+    }
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb) {
+        const int r = wm * C::TM + mb * 16 + i16;
+        f.t[mb] = *reinterpret_cast<const bf16x8_t*>(&as[a_slot<16>(r, g16) * 8]);
+    }
+}
+
+template <class C>
+__device__ __forceinline__ void mfma_step16(f32x4_t (&acc)[C::MB][C::NB], const Frags16<C>& f) {
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.w[nb], f.t[mb], acc[mb][nb], 0, 0, 0);
+}
+
+// accumulator [mb][nb] of lane l: row 16 mb + l % 16, columns 16 nb + 4 (l / 16)..+3
+template <class C, int EPI>
+__device__ __forceinline__ void epilogue16(const GemmArgs& g, const Item<C>& it, const f32x4_t (&acc)[C::MB][C::NB],
+                                           const f32x4_t (&bias4)[C::NB], int wm, int wn, int lane) {
+    const int g16 = lane >> 4, i16 = lane & 15;
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb) {
+        const int ml = wm * C::TM + mb * 16 + i16;
+        if (ml >= it.mrows) continue;
+        const int64_t row = it.m0 + ml;
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb) {
+            const int n = it.n0 + wn * C::TN + nb * 16 + 4 * g16;
+            if (n >= g.N) continue;
+            store4<EPI>(g, row, n, acc[mb][nb] + bias4[nb]);
+        }
+    }
+}
+
+// ---- 32x32x16 fragments (large tiles) ------------------------------------
+// One K-step = two K-halves of 16.  Weight fragment [nb][h]: lane l holds
+// column 32 nb + l % 32, K 16 h + 8 (l / 32)..+7; activation fragment
+// [mb][h]: row 32 mb + l % 32, the same K.
+template <class C>
+struct Frags32 {
+    bf16x8_t w[C::NB][2];
+    bf16x8_t t[C::MB][2];
+};
+
+template <class C>
+__device__ __forceinline__ void read_frags32(Frags32<C>& f, const uint16_t* as, const uint16_t* bs, int wm, int wn,
+                                             int lane) {
+    const int g16 = lane >> 4, i16 = lane & 15;
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            // the 16-lane group g16 covers columns 16 (g16 & 1)..+15 of the block and
+            // K rows 16 h + 8 (g16 >> 1)..+7: lane i16 points at row (i16 >> 2) (+4),
+            // columns 4 (i16 & 3)..+3 of that 4 x 16 window
+            const int col = wn * C::TN + nb * 32 + 16 * (g16 & 1) + 4 * (i16 & 3);
+            const int k = 16 * h + 8 * (g16 >> 1) + (i16 >> 2);
+            const int c = col >> 3, half = (col & 7);
+            const bf16x4_t lo = lds_read_tr(&bs[k * C::BN + b_chunk<32>(k, c) * 8 + half]);
+            const bf16x4_t hi = lds_read_tr(&bs[(k + 4) * C::BN + b_chunk<32>(k + 4, c) * 8 + half]);
+            f.w[nb][h] = cat8(lo, hi);
+        }
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int r = wm * C::TM + mb * 32 + (lane & 31);
+            f.t[mb][h] = *reinterpret_cast<const bf16x8_t*>(&as[a_slot<32>(r, 2 * h + (lane >> 5)) * 8]);
+        }
+}
+
+// the MFMAs of K-half h of one step
+template <class C>
+__device__ __forceinline__ void mfma_half32(f32x16_t (&acc)[C::MB][C::NB], const Frags32<C>& f, int h) {
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.w[nb][h], f.t[mb][h], acc[mb][nb], 0, 0, 0);
+}
+
+// accumulator [mb][nb] of lane l, elements 4q..4q+3: row 32 mb + l % 32,
+// columns 32 nb + 8 q + 4 (l / 32)..+3; bias from the item's LDS slice, one
+// quad live at a time
+template <class C, int EPI>
+__device__ __forceinline__ void epilogue32(const GemmArgs& g, const Item<C>& it, const f32x16_t (&acc)[C::MB][C::NB],
+                                           const float* sbias, int wm, int wn, int lane) {
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int nl = wn * C::TN + nb * 32 + 8 * q + 4 * (lane >> 5);
+            const int n = it.n0 + nl;
+            if (n >= g.N) continue;
+            const f32x4_t b = *reinterpret_cast<const f32x4_t*>(&sbias[nl]);
+#pragma unroll
+            for (int mb = 0; mb < C::MB; ++mb) {
+                const int ml = wm * C::TM + mb * 32 + (lane & 31);
+                if (ml >= it.mrows) continue;
+                const f32x4_t v = {acc[mb][nb][4 * q], acc[mb][nb][4 * q + 1], acc[mb][nb][4 * q + 2],
+                                   acc[mb][nb][4 * q + 3]};
+                store4<EPI>(g, it.m0 + ml, n, v + b);
+            }
+        }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Small tiles: every wave reads and multiplies each step; one s_waitcnt
+// vmcnt + s_barrier per step publishes the oldest stage and frees the one
+// consumed before it.
+template <class C, int EPI>
+__global__ __launch_bounds__(C::NT) void ffn_gemm_bf16_kernel(GemmArgs g) {
+    static_assert(C::MF == 16, "small tiles use the 16x16x32 form");
+    __shared__ __attribute__((aligned(1024))) uint16_t sa[NSTAGE][C::BM * BK];
+    __shared__ __attribute__((aligned(1024))) uint16_t sb[NSTAGE][BK * C::BN];
+    __shared__ int mt_pre[1025];
+    __shared__ int s_off[1025];
+    __shared__ int scan_tmp[32];
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wid = tid / kWave;
+    const int wm = wid / C::WN, wn = wid % C::WN;
+    const int g16 = lane >> 4;
+    const int E = g.E, K = g.K, N = g.N;
+    const int ntn = (N + C::BN - 1) / C::BN;
+    const int nk = (K + BK - 1) / BK;
+
+    for (int i = tid; i <= E; i += C::NT) s_off[i] = g.offsets[i];
+    const int total_mt = build_mtile_prefix(g.offsets, E, C::BM, mt_pre, scan_tmp);   // ends with a barrier
+    const ItemRange range = xcd_item_range((int64_t)total_mt * ntn);
+    if (range.first >= range.end) return;
+    const Loader<C> ld(g, s_off, mt_pre, ntn, wid, lane);
 
     constexpr int PER = C::A_DMA + C::B_DMA;   // vector-memory ops per stage per lane
     int64_t item = range.first;
-    Item cur;
-    setup(item, cur);
-    prologue(cur);
+    Item<C> cur;
+    ld.setup(item, cur);
+    for (int s = 0; s < NSTAGE - 1 && s < nk; ++s) ld.issue(cur, s, sa[s], sb[s]);
     while (true) {
         f32x4_t acc[C::MB][C::NB];
 #pragma unroll
@@ -215,99 +446,180 @@ __global__ __launch_bounds__(C::NT) void ffn_gemm_bf16_kernel(GemmArgs g) {
             if (kt == 0 || ahead == 0) wait_vm_barrier<0>();   // first step: epilogue stores may be in flight
             else if (ahead >= 2) wait_vm_barrier<2 * PER>();
             else wait_vm_barrier<PER>();
-            if (kt + NSTAGE - 1 < nk) issue(cur, kt + NSTAGE - 1);
-            const uint16_t* as = sa[kt % NSTAGE];
-            const uint16_t* bs = sb[kt % NSTAGE];
-            bf16x8_t wf[C::NB];
-#pragma unroll
-            for (int nb = 0; nb < C::NB; ++nb) {
-                // rows 8 g16 + (i16 >> 2) (+4), columns 4 (i16 & 3) of the 16-column block
-                const int col = wn * C::TN + nb * 16 + 4 * (i16 & 3);
-                const int k = 8 * g16 + (i16 >> 2);
-                const int c = col >> 3, half = (col & 7);
-                const bf16x4_t lo = lds_read_tr(&bs[k * C::BN + b_chunk(k, c) * 8 + half]);
-                const bf16x4_t hi = lds_read_tr(&bs[(k + 4) * C::BN + b_chunk(k + 4, c) * 8 + half]);
-                wf[nb] = cat8(lo, hi);
+            if (kt + NSTAGE - 1 < nk) {
+                const int b = (kt + NSTAGE - 1) % NSTAGE;
+                ld.issue(cur, kt + NSTAGE - 1, sa[b], sb[b]);
             }
-#pragma unroll
-            for (int mb = 0; mb < C::MB; ++mb) {
-                const int r = wm * C::TM + mb * 16 + i16;
-                const bf16x8_t tf = *reinterpret_cast<const bf16x8_t*>(&as[a_slot(r, g16) * 8]);
-#pragma unroll
-                for (int nb = 0; nb < C::NB; ++nb)
-                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[nb], tf, acc[mb][nb], 0, 0, 0);
-            }
+            Frags16<C> f;
+            read_frags16<C>(f, sa[kt % NSTAGE], sb[kt % NSTAGE], wm, wn, lane);
+            mfma_step16<C>(acc, f);
         }
         // every wave is done reading the ring and every load has landed
         wait_vm_barrier<0>();
 
         // epilogue inputs first (global loads), then the next item's first
         // stages, then the epilogue arithmetic and stores overlap those loads
-        float4 bias4[C::NB];
+        f32x4_t bias4[C::NB];
 #pragma unroll
         for (int nb = 0; nb < C::NB; ++nb) {
+            // clamped into the row for a column tail; those columns are never stored
             const int n = min(cur.n0 + wn * C::TN + nb * 16 + 4 * g16, N - 4);
-            bias4[nb] = *reinterpret_cast<const float4*>(g.bias + (int64_t)cur.e * N + n);
+            bias4[nb] = *reinterpret_cast<const f32x4_t*>(g.bias + (int64_t)cur.e * N + n);
         }
-        const Item done = cur;
+        const Item<C> done = cur;
         const int64_t next = item + range.step;
         const bool more = next < range.end;
         if (more) {
             // keep the epilogue's loads out of the DMA's vmcnt window
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            setup(next, cur);
-            prologue(cur);
+            ld.setup(next, cur);
+            for (int s = 0; s < NSTAGE - 1 && s < nk; ++s) ld.issue(cur, s, sa[s], sb[s]);
         }
-
-#pragma unroll
-        for (int mb = 0; mb < C::MB; ++mb) {
-            const int ml = wm * C::TM + mb * 16 + i16;
-            if (ml >= done.mrows) continue;
-            const int64_t row = done.m0 + ml;
-#pragma unroll
-            for (int nb = 0; nb < C::NB; ++nb) {
-                const int n = done.n0 + wn * C::TN + nb * 16 + 4 * g16;
-                if (n >= N) continue;
-                const float4 bv = bias4[nb];
-                const float v0 = acc[mb][nb][0] + bv.x, v1 = acc[mb][nb][1] + bv.y;
-                const float v2 = acc[mb][nb][2] + bv.z, v3 = acc[mb][nb][3] + bv.w;
-                if constexpr (EPI == EPI_GELU_H) {
-                    uint2 pk;
-                    pk.x = (uint32_t)f32_to_bf16_bits(gelu_as(v0)) |
-                           ((uint32_t)f32_to_bf16_bits(gelu_as(v1)) << 16);
-                    pk.y = (uint32_t)f32_to_bf16_bits(gelu_as(v2)) |
-                           ((uint32_t)f32_to_bf16_bits(gelu_as(v3)) << 16);
-                    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(g.out) + row * N + n) = pk;
-                } else {
-                    *reinterpret_cast<float4*>(static_cast<float*>(g.out) + row * N + n) =
-                        make_float4(v0, v1, v2, v3);
-                }
-            }
-        }
+        epilogue16<C, EPI>(g, done, acc, bias4, wm, wn, lane);
         if (!more) break;
         item = next;
     }
 }
 
-template <class C, int EPI>
-static int persistent_blocks() {
-    static int blocks = 0;
-    if (blocks == 0) {
-        int per_cu = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ffn_gemm_bf16_kernel<C, EPI>, C::NT, 0) !=
-                hipSuccess ||
-            per_cu < 1)
-            per_cu = 1;
-        blocks = per_cu * device_cu_count();
-        if (blocks < kXcds) blocks = kXcds;
+// ---------------------------------------------------------------------------
+// Large tiles, pipelined: each wave reads the next step's fragments from LDS
+// into a second register set while its MFMAs run on the current set.
+//
+// The ring of NS slots runs on across items (the next item's loads start
+// while the current one finishes; past the last item out-of-range loads keep
+// every wave's count per step at PER).  Items take an even number of steps
+// (an odd K-step count gets one all-zero step), so the two fragment sets
+// swap roles in a loop unrolled by two.  Global step j:
+//   * opens with vmcnt((NS-2) PER) lgkmcnt(0) and the barrier: stage j+1
+//     (read during step j) has landed for every wave; the fragments of step
+//     j are in registers, so slot j % NS is free for every wave;
+//   * issues stage j+NS into that slot, reads stage j+1 into the other set,
+//     multiplies the current set.
+// Wave 0 loads each item's bias slice into LDS with the item's first stage
+// (one extra load only makes that wave's later vmcnt waits stricter), so no
+// global load in the loop leaves the compiler to insert a wait for every
+// load in flight.  The load cursor runs NS steps ahead; an item has two
+// steps or more, so it is at most ceil(NS / 2) items ahead and NS bias slots
+// (NS >= 3) never overwrite one still in use.
+//
+// WPE: waves per SIMD the kernel is built for (register budget 512 / WPE).
+template <class C, int NS, int EMAX, int WPE, int EPI>
+__global__ __launch_bounds__(C::NT, WPE) void ffn_gemm_bf16_pipe_kernel(GemmArgs g) {
+    static_assert(C::MF == 32 && C::BN == 256, "256-column tiles on 32x32x16 MFMAs");
+    static_assert(NS >= 3 && NS <= 4, "ring depth");
+    __shared__ __attribute__((aligned(1024))) uint16_t sa[NS][C::BM * BK];
+    __shared__ __attribute__((aligned(1024))) uint16_t sb[NS][BK * C::BN];
+    __shared__ int mt_pre[EMAX + 1];
+    __shared__ int s_off[EMAX + 1];
+    __shared__ int scan_tmp[32];
+    __shared__ __attribute__((aligned(16))) float s_bias[NS][C::BN];   // by item number mod NS
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform: scalar branches
+    const int wm = wid / C::WN, wn = wid % C::WN;
+    const int E = g.E, K = g.K, N = g.N;
+    const int ntn = (N + C::BN - 1) / C::BN;
+    const int nk = (K + BK - 1) / BK;
+    const int nks = nk + (nk & 1);   // steps per item, even
+
+    for (int i = tid; i <= E; i += C::NT) s_off[i] = g.offsets[i];
+    const int total_mt = build_mtile_prefix(g.offsets, E, C::BM, mt_pre, scan_tmp);   // ends with a barrier
+    const ItemRange range = xcd_item_range((int64_t)total_mt * ntn);
+    if (range.first >= range.end) return;
+    const Loader<C> ld(g, s_off, mt_pre, ntn, wid, lane);
+    constexpr int PER = C::A_DMA + C::B_DMA;
+
+    // load cursor: item, K-step, ring slot and bias slot of the next stage
+    Item<C> lit;
+    int64_t l_item = range.first;
+    int l_kt = 0, l_slot = 0, l_bslot = 0;
+    ld.setup(l_item, lit);
+    auto issue_next = [&]() {
+        if (l_item < range.end) {
+            if (l_kt == 0 && wid == 0) ld.issue_bias(lit, g.bias, lane, s_bias[l_bslot]);
+            if (l_kt < nk) ld.issue(lit, l_kt, sa[l_slot], sb[l_slot]);
+            else ld.issue_zero(lit, sa[l_slot], sb[l_slot]);
+        } else {
+            ld.issue_zero(lit, sa[l_slot], sb[l_slot]);
+        }
+        if (++l_slot == NS) l_slot = 0;
+        if (++l_kt == nks) {
+            l_kt = 0;
+            if (++l_bslot == NS) l_bslot = 0;
+            l_item += range.step;
+            if (l_item < range.end) ld.setup(l_item, lit);
+        }
+    };
+    for (int s = 0; s < NS; ++s) issue_next();
+    pipe_barrier<(NS - 1) * PER>();   // stage 0 landed everywhere
+
+    Frags32<C> fa, fb;
+    read_frags32<C>(fa, sa[0], sb[0], wm, wn, lane);
+    int c_slot = 0, c_bslot = 0;
+    int64_t item = range.first;
+    f32x16_t acc[C::MB][C::NB];
+    auto step = [&](Frags32<C>& cur, Frags32<C>& nxt) {
+        pipe_barrier<(NS - 2) * PER>();
+        const int ns = c_slot + 1 == NS ? 0 : c_slot + 1;
+        // all next-step reads first (they return while the MFMAs run), then the
+        // first K-half of MFMAs, then this step's global -> LDS loads, then the
+        // second K-half: the loads of eight waves take the TA ~500 cycles per
+        // step, and issued right after the barrier they held back the MFMAs
+        read_frags32<C>(nxt, sa[ns], sb[ns], wm, wn, lane);
+        mfma_half32<C>(acc, cur, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4 * C::NB + 2 * C::MB, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, C::MB * C::NB, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        issue_next();
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_half32<C>(acc, cur, 1);
+        c_slot = ns;
+    };
+    while (true) {
+        Item<C> cur;
+        ld.decode(item, cur);
+#pragma unroll
+        for (int i = 0; i < C::MB; ++i)
+#pragma unroll
+            for (int j = 0; j < C::NB; ++j)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+        for (int kt = 0; kt < nks; kt += 2) {
+            step(fa, fb);
+            step(fb, fa);
+        }
+        // the bias slice landed with the item's first stage, several barriers ago
+        epilogue32<C, EPI>(g, cur, acc, s_bias[c_bslot], wm, wn, lane);
+        if (++c_bslot == NS) c_bslot = 0;
+        item += range.step;
+        if (item >= range.end) break;
     }
-    return blocks;
+    // the trailing out-of-range loads still write the ring
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+template <class KernelFn>
+static int persistent_blocks(KernelFn kernel, int threads) {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess || per_cu < 1)
+        per_cu = 1;
+    const int blocks = per_cu * device_cu_count();
+    return blocks < kXcds ? kXcds : blocks;
 }
 
 template <class C, int EPI>
-static hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
-    hipLaunchKernelGGL((ffn_gemm_bf16_kernel<C, EPI>), dim3(persistent_blocks<C, EPI>()), dim3(C::NT), 0, st, g);
-    return hipGetLastError();
+static int small_blocks() {
+    static const int blocks = persistent_blocks(ffn_gemm_bf16_kernel<C, EPI>, C::NT);
+    return blocks;
+}
+
+// Large tiles: 256 x 256 on eight waves (two per SIMD), four 32 KiB stages.
+// (Two workgroups per CU on 128 x 256 tiles measured slower where weight
+// tiles are shared by several m-tiles: each re-reads them from HBM.)
+template <class C, int NS, int EMAX, int WPE, int EPI>
+static int pipe_blocks() {
+    static const int blocks = persistent_blocks(ffn_gemm_bf16_pipe_kernel<C, NS, EMAX, WPE, EPI>, C::NT);
+    return blocks;
 }
 
 // Upper bound of the work items for tile C: every expert may add one
@@ -317,12 +629,23 @@ static int64_t item_bound(const GemmArgs& g, int64_t max_rows) {
     return ((max_rows + C::BM - 1) / C::BM + g.E) * ((g.N + C::BN - 1) / C::BN);
 }
 
+template <class C, int NS, int EMAX, int WPE, int EPI>
+static bool try_pipe(const GemmArgs& g, int64_t max_rows, hipStream_t st, hipError_t* err) {
+    const int blocks = pipe_blocks<C, NS, EMAX, WPE, EPI>();
+    // large tiles need about 3 items per workgroup to keep the tail short
+    if (g.E > EMAX || item_bound<C>(g, max_rows) < 3 * (int64_t)blocks) return false;
+    hipLaunchKernelGGL((ffn_gemm_bf16_pipe_kernel<C, NS, EMAX, WPE, EPI>), dim3(blocks), dim3(C::NT), 0, st, g);
+    *err = hipGetLastError();
+    return true;
+}
+
 template <int EPI>
 static hipError_t launch_epi(const GemmArgs& g, int64_t max_rows, hipStream_t st) {
-    // large tiles need about 3 items per CU to keep the tail short
-    const int64_t large = item_bound<TileLarge>(g, max_rows);
-    if (large >= 3 * (int64_t)persistent_blocks<TileLarge, EPI>()) return launch_cfg<TileLarge, EPI>(g, st);
-    return launch_cfg<TileSmall, EPI>(g, st);
+    hipError_t err = hipSuccess;
+    if (try_pipe<TilePipe, 4, 1024, 2, EPI>(g, max_rows, st, &err)) return err;
+    hipLaunchKernelGGL((ffn_gemm_bf16_kernel<TileSmall, EPI>), dim3(small_blocks<TileSmall, EPI>()),
+                       dim3(TileSmall::NT), 0, st, g);
+    return hipGetLastError();
 }
 
 hipError_t launch_ffn_gemm_bf16(const GemmArgs& g, int epi, int64_t max_rows, hipStream_t st) {

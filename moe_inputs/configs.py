@@ -114,6 +114,15 @@ _add(MoEConfig("cap_one", T=200, d=64, E=8, k=2, d_ff=64,
                capacity_factor=0.02, bias_std=0.1,
                note="capacity clips to 1 slot per expert"))
 
+# the 256 x 256 tile path with ragged tails: d and d_ff are multiples of
+# neither the 32-wide K step nor the 256-wide N tile, uneven expert loads
+_add(MoEConfig("ragged_large", T=16384, d=1800, E=8, k=2, d_ff=2000,
+               capacity_factor=1.1, bias_std=0.1, gate_bias_std=0.5,
+               note="odd K-step counts (57, 63): one all-zero step per item"))
+_add(MoEConfig("ragged_large_even", T=32768, d=1000, E=8, k=2, d_ff=1976,
+               capacity_factor=1.1, bias_std=0.1, gate_bias_std=0.5,
+               note="even K-step counts (32, 62) with a partial last step"))
+
 # limits of the library: E = 1024 experts, k = 32 choices per token
 _add(MoEConfig("max_experts", T=2048, d=64, E=1024, k=4, d_ff=64,
                capacity_factor=1.0, bias_std=0.1))
