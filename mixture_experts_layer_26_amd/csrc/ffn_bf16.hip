@@ -35,6 +35,7 @@
 //   * small problems: 128 x 128 tiles, four waves on v_mfma_f32_16x16x32_bf16,
 //     one barrier per step (read, then multiply).
 #include "ffn_sched.h"
+#include "lds_dma.h"
 #include "moe_kernels.h"
 
 namespace moe {
@@ -72,30 +73,7 @@ struct TileCfg {
 using TileSmall = TileCfg<MOE_TILE_SMALL>;
 using TilePipe = TileCfg<MOE_TILE_PIPE>;
 
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-
-// 16 bytes per lane, global -> LDS at (lds + 16 * lane).  Issued as inline asm
-// so that the compiler's wait insertion neither tracks it nor adds vmcnt
-// waits for it: every wait on these loads is explicit.
-__device__ __forceinline__ void dma16(const i32x4_t& rsrc, const void* lds, int voffset) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds));
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :: "s"(m0), "v"(voffset), "s"(rsrc) : "memory", "m0");
-}
-
-// Buffer descriptor: 48-bit base, stride 0, range in bytes, gfx9 data format.
-__device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t bytes) {
-    const uint64_t a = reinterpret_cast<uint64_t>(base);
-    i32x4_t r;
-    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-    r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xffff);
-    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
-    r[3] = 0x00020000;
-    return r;
-}
-
-constexpr int kOutOfRange = 0x7ff00000;   // byte offset past any range: reads zeros
 
 __device__ __forceinline__ bf16x4_t lds_read_tr(const uint16_t* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MOE_LDS bf16x4_t*)(p));
@@ -138,22 +116,8 @@ __device__ __forceinline__ void wait_vm_barrier() {
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-// s_waitcnt immediate (gfx9 layout: vmcnt in bits 3:0 and 15:14, expcnt 6:4,
-// lgkmcnt 11:8); expcnt is never waited on here
-constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
-
-// vmcnt(VM) lgkmcnt(0) then the workgroup barrier.  The wait goes through the
-// builtin so the compiler's own wait insertion knows every LDS read has
-// returned; the barrier is asm with a memory clobber so no LDS access moves
-// across it, and the scheduling barriers keep the MFMAs of a step inside it.
 template <int VM>
-__device__ __forceinline__ void pipe_barrier() {
-    static_assert(VM >= 0 && VM < 64, "vmcnt range");
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(VM, 0));
-    asm volatile("s_barrier" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-}
+__device__ __forceinline__ void pipe_barrier() { dma_barrier<VM>(); }
 
 // fp32 pair -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {

@@ -11,23 +11,23 @@
 // fp32 accumulation, like an fp32 FMA chain (the order of the additions
 // differs).
 //
-// split_gate_kernel writes the three parts once per call, [3][d][EP2] with
-// the expert dimension zero-padded to a power of two EP2 >= 16.
-// route_mfma_kernel<EP2, BM>: one workgroup owns BM tokens and all experts;
-// K-steps of 32 staged global -> registers -> LDS (two buffers); the four
-// waves split the expert columns (and the token rows when EP2 < 64).  The
-// logit tile goes to LDS, then groups of G = EP2/4 lanes select the top k of
-// each token with butterfly arg-max reductions of compile-time width.
-#include "moe_common.h"
+// split_gate_kernel writes the three parts once per call, expert-major and
+// K-contiguous: [3][EP2][d], the expert dimension zero-padded to a power of
+// two EP2 >= 16.
+// route_mfma_kernel<EP2, BM, NS, KS>: one workgroup owns BM tokens and all
+// experts.  Each K-step of 32 puts BM token rows and 3 EP2 weight rows of 64
+// bytes global -> LDS (buffer_load ... lds); a stage of KS K-steps goes
+// through a ring of NS slots, so NS-1 stages of loads are in flight; both
+// operands are read back with ds_read_b128 from the same swizzled layout.  The four waves split the
+// expert columns (and the token rows when EP2 < 64).  The logit tile goes to
+// LDS, then groups of G = min(16, EP2/4) lanes select the top k of each
+// token with arg-max reductions over DPP lane moves.
+#include "lds_dma.h"
 #include "moe_kernels.h"
 
 namespace moe {
 
 namespace {
-
-__device__ __forceinline__ bf16x4_t lds_tr(const uint16_t* p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MOE_LDS bf16x4_t*)(p));
-}
 
 __device__ __forceinline__ bool beats(float av, int ai, float bv, int bi) {
     return av > bv || (av == bv && ai < bi);
@@ -39,8 +39,8 @@ __global__ __launch_bounds__(256) void split_gate_kernel(const float* __restrict
                                                          uint16_t* __restrict__ W3) {
     const int64_t n = (int64_t)d * EP2;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t kk = i / EP2;
-        const int e = (int)(i - kk * EP2);
+        const int e = (int)(i / d);
+        const int64_t kk = i - (int64_t)e * d;
         const float w = e < E ? Wg[kk * E + e] : 0.0f;
         const uint16_t hi = f32_to_bf16_bits(w);
         const float r1 = w - bf16_bits_to_f32(hi);     // exact
@@ -52,12 +52,32 @@ __global__ __launch_bounds__(256) void split_gate_kernel(const float* __restrict
     }
 }
 
-// Top-k + softmax of one token's logits row[0..E) by a group of G lanes.
-// Lane gl holds row[gl + G*i], i < NV (E <= G*NV).  Every lane of the wave
-// calls this; only active groups write.  Ties go to the lower expert index.
+// Cross-lane moves inside a row of 16 lanes (DPP: no LDS round trip).
+// Step 0 pairs lanes 4q+{0,1},{2,3}; step 1 pairs 4q+{0,2},{1,3}; step 2
+// mirrors the two quads of each 8 (i <-> 7-i); step 3 mirrors the two
+// halves of each 16 (i <-> 15-i).  Each pairing is symmetric and joins two
+// disjoint sets whose union is the next power-of-two group, so steps 0..s
+// all-reduce groups of 2^(s+1) lanes.
+template <int STEP>
+__device__ __forceinline__ int dpp_partner(int v) {
+    constexpr int ctrl = STEP == 0 ? 0xB1 : STEP == 1 ? 0x4E : STEP == 2 ? 0x141 : 0x140;
+    return __builtin_amdgcn_mov_dpp(v, ctrl, 0xF, 0xF, false);
+}
+template <int STEP>
+__device__ __forceinline__ float dpp_partner(float v) {
+    return __int_as_float(dpp_partner<STEP>(__float_as_int(v)));
+}
+
+// Top-k + softmax of one token's logits row[0..E) by a group of G lanes
+// (G = 4, 8 or 16, aligned inside a row of 16).  Lane gl holds
+// row[gl + G*i], i < NV (E <= G*NV); round r takes the best value not yet
+// taken (ties to the lower expert index) and lane r keeps it.  Every lane of
+// the wave calls this; only active groups write.
 template <int G, int NV>
 __device__ __forceinline__ void topk_group(const float* row, int E, int k, float tau, int gl, bool active,
                                            int32_t* idx_out, float* w_out) {
+    static_assert(G == 4 || G == 8 || G == 16, "group inside a DPP row");
+    constexpr int STEPS = G == 4 ? 2 : G == 8 ? 3 : 4;
     float v[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
@@ -65,7 +85,7 @@ __device__ __forceinline__ void topk_group(const float* row, int E, int k, float
         v[i] = (e < E) ? row[e] : -INFINITY;
     }
     uint32_t taken = 0;
-    float my_v = 0.0f;
+    float my_v = 0.0f, top = 0.0f;
     int my_i = 0;
     for (int r = 0; r < k; ++r) {
         float bv = -INFINITY;
@@ -79,33 +99,45 @@ __device__ __forceinline__ void topk_group(const float* row, int E, int k, float
             }
         }
 #pragma unroll
-        for (int off = G / 2; off > 0; off >>= 1) {
-            const float ov = __shfl_xor(bv, off, kWave);
-            const int oi = __shfl_xor(bi, off, kWave);
+        for (int st = 0; st < STEPS; ++st) {
+            float ov;
+            int oi;
+            switch (st) {
+                case 0: ov = dpp_partner<0>(bv); oi = dpp_partner<0>(bi); break;
+                case 1: ov = dpp_partner<1>(bv); oi = dpp_partner<1>(bi); break;
+                case 2: ov = dpp_partner<2>(bv); oi = dpp_partner<2>(bi); break;
+                default: ov = dpp_partner<3>(bv); oi = dpp_partner<3>(bi); break;
+            }
             if (beats(ov, oi, bv, bi)) {
                 bv = ov;
                 bi = oi;
             }
         }
         if ((bi & (G - 1)) == gl) taken |= 1u << (bi / G);
+        if (r == 0) top = bv;
         if (gl == r) {
             my_v = bv;
             my_i = bi;
         }
     }
-    const int lane = threadIdx.x & (kWave - 1);
-    const float top = __shfl(my_v, lane & ~(G - 1), kWave);
-    float p = (gl < k) ? expf((my_v - top) / tau) : 0.0f;
+    const float p = (gl < k) ? expf((my_v - top) / tau) : 0.0f;
     float z = p;
 #pragma unroll
-    for (int off = G / 2; off > 0; off >>= 1) z += __shfl_xor(z, off, kWave);
+    for (int st = 0; st < STEPS; ++st) {
+        switch (st) {
+            case 0: z += dpp_partner<0>(z); break;
+            case 1: z += dpp_partner<1>(z); break;
+            case 2: z += dpp_partner<2>(z); break;
+            default: z += dpp_partner<3>(z); break;
+        }
+    }
     if (active && gl < k) {
         idx_out[gl] = my_i;
         w_out[gl] = p / z;
     }
 }
 
-template <int EP2, int BM>
+template <int EP2, int BM, int NS, int KS>
 __global__ __launch_bounds__(256) void route_mfma_kernel(RouteArgs a, const uint16_t* __restrict__ W3) {
     constexpr int BKG = 32;
     constexpr int WN = EP2 / 16 >= 4 ? 4 : EP2 / 16;  // waves across experts
@@ -113,69 +145,55 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(RouteArgs a, const uint
     constexpr int NBW = EP2 / 16 / WN;                  // 16-expert blocks per wave
     constexpr int MBW = BM / 16 / WM;                   // 16-token blocks per wave
     static_assert(MBW >= 1 && NBW >= 1, "tile too small for four waves");
-    constexpr int XP = BKG + 8;          // LDS pitch of the token tile (elements)
-    constexpr int WP = EP2 + 8;          // LDS pitch of a weight tile
-    constexpr int XCH = BM * BKG / 8;    // 16-byte chunks of the token tile
-    constexpr int WCH = 3 * BKG * EP2 / 8;
-    constexpr int LX = (XCH + 255) / 256, LW = (WCH + 255) / 256;
+    constexpr int ROWS = BM + 3 * EP2;       // 64-byte rows per K-step: tokens, then weight parts
+    constexpr int INSTR1 = ROWS / 16;        // 1 KiB wave loads per K-step
+    constexpr int INSTR = KS * INSTR1;       // per stage of KS K-steps
+    constexpr int PER = (INSTR + 3) / 4;     // per wave; the ones past INSTR fill unused rows
+    constexpr int STAGE = 4 * PER * 512;     // bf16 elements per slot
     constexpr int LTP = EP2 + 1;
-    struct Smem {
-        uint16_t xs[2][BM * XP];
-        uint16_t ws[2][3 * BKG * WP];
-    };
-    __shared__ __attribute__((aligned(16))) union {
-        Smem s;
+    static_assert(BM % 16 == 0, "token rows in whole wave loads");
+    static_assert((NS - 2) * PER < 64, "vmcnt range");
+    static_assert(NS * STAGE * 2 <= 160 * 1024 && BM * LTP * 4 <= 160 * 1024, "LDS of one CU");
+    __shared__ __attribute__((aligned(1024))) union {
+        uint16_t ring[NS][STAGE];
         float lt[BM * LTP];
     } sm;
 
-    const uint16_t* __restrict__ x = static_cast<const uint16_t*>(a.x);
     const int64_t T = a.T;
     const int d = a.d, E = a.E;
     const int64_t t0 = (int64_t)blockIdx.x * BM;
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wid / WN, wn = wid % WN;
     const int g16 = lane >> 4, i16 = lane & 15;
-    const int64_t nW = (int64_t)d * EP2;
-    const int nk = (d + BKG - 1) / BKG;
+    const int nk = (d + BKG - 1) / BKG;          // K-steps
+    const int nst = (nk + KS - 1) / KS;          // stages
 
-    uint4 rx[LX], rw[LW];
-    auto load = [&](int kt) {
-        const int k0 = kt * BKG;
+    // load geometry of this lane: wave load j = wid * PER + i covers K-step
+    // j / INSTR1 of the stage, tile rows 16 (j % INSTR1) .. +15; lane -> row
+    // 16 (j % INSTR1) + lane / 4, physical slot lane % 4, logical chunk
+    // c = slot ^ swz(row), i.e. K offset 8 c of that K-step
+    const int64_t valid = T - t0 < BM ? T - t0 : BM;
+    const i32x4_t rsx = make_rsrc(static_cast<const uint16_t*>(a.x) + t0 * d, (uint32_t)(valid * d * 2));
+    const i32x4_t rsw = make_rsrc(W3, (uint32_t)(3u * EP2 * (uint32_t)d * 2u));
+    int base[PER], c8[PER];
 #pragma unroll
-        for (int j = 0; j < LX; ++j) {
-            const int c = tid + 256 * j;
-            if (c < XCH) {
-                const int r = c >> 2, kc = (c & 3) * 8;
-                const int64_t t = t0 + r;
-                rx[j] = (t < T && k0 + kc < d) ? *reinterpret_cast<const uint4*>(x + t * d + k0 + kc)
-                                               : make_uint4(0u, 0u, 0u, 0u);
-            }
-        }
+    for (int i = 0; i < PER; ++i) {
+        const int j = wid * PER + i;
+        const int r = 16 * (j % INSTR1) + (lane >> 2);
+        const int c = (lane & 3) ^ k64_swz(r);
+        const int src_row = r < BM ? r : r - BM;    // token row of the block, or weight row s * EP2 + e
+        base[i] = (src_row * d + 8 * c + BKG * (j / INSTR1)) * 2;
+        c8[i] = 8 * c + BKG * (j / INSTR1);
+    }
+    auto issue = [&](int st, int slot) {   // st >= nst: every load out of range
+        const int k0 = st * KS * BKG;
 #pragma unroll
-        for (int j = 0; j < LW; ++j) {
-            const int c = tid + 256 * j;
-            if (c < WCH) {
-                const int s = c / (BKG * EP2 / 8), rem = c % (BKG * EP2 / 8);
-                const int kk = rem / (EP2 / 8), ec = (rem % (EP2 / 8)) * 8;
-                rw[j] = (k0 + kk < d) ? *reinterpret_cast<const uint4*>(W3 + s * nW + (int64_t)(k0 + kk) * EP2 + ec)
-                                      : make_uint4(0u, 0u, 0u, 0u);
-            }
-        }
-    };
-    auto store = [&](int buf) {
-#pragma unroll
-        for (int j = 0; j < LX; ++j) {
-            const int c = tid + 256 * j;
-            if (c < XCH) *reinterpret_cast<uint4*>(&sm.s.xs[buf][(c >> 2) * XP + (c & 3) * 8]) = rx[j];
-        }
-#pragma unroll
-        for (int j = 0; j < LW; ++j) {
-            const int c = tid + 256 * j;
-            if (c < WCH) {
-                const int s = c / (BKG * EP2 / 8), rem = c % (BKG * EP2 / 8);
-                const int kk = rem / (EP2 / 8), ec = (rem % (EP2 / 8)) * 8;
-                *reinterpret_cast<uint4*>(&sm.s.ws[buf][(s * BKG + kk) * WP + ec]) = rw[j];
-            }
+        for (int i = 0; i < PER; ++i) {
+            const int j = wid * PER + i;
+            const bool ok = j < INSTR && st < nst && k0 + c8[i] < d;
+            const int off = ok ? base[i] + 2 * k0 : kOutOfRange;
+            dma16(16 * (j % INSTR1) < BM ? rsx : rsw, &sm.ring[slot][j * 512], off);
         }
     };
 
@@ -185,35 +203,43 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(RouteArgs a, const uint
 #pragma unroll
         for (int j = 0; j < NBW; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    load(0);
-    store(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) load(kt + 1);
-        const uint16_t* xs = sm.s.xs[cur];
-        const uint16_t* wsb = sm.s.ws[cur];
-        bf16x8_t xf[MBW];
+    for (int s = 0; s < NS - 1; ++s) issue(s, s);
+    int slot = 0;
+    for (int st = 0; st < nst; ++st) {
+        // stage st has landed for every wave; slot (st - 1) % NS is free
+        dma_barrier<(NS - 2) * PER>();
+        issue(st + NS - 1, slot == 0 ? NS - 1 : slot - 1);
+        const uint16_t* sp = sm.ring[slot];
+        // every fragment of the stage first, then the MFMAs
+        bf16x8_t xf[KS][MBW], wf[KS][3][NBW];
 #pragma unroll
-        for (int mb = 0; mb < MBW; ++mb)
-            xf[mb] = *reinterpret_cast<const bf16x8_t*>(&xs[((wm * MBW + mb) * 16 + i16) * XP + 8 * g16]);
+        for (int q = 0; q < KS; ++q) {
+            const uint16_t* sq = sp + q * INSTR1 * 512;
 #pragma unroll
-        for (int s = 0; s < 3; ++s) {
+            for (int mb = 0; mb < MBW; ++mb)
+                xf[q][mb] = *reinterpret_cast<const bf16x8_t*>(&sq[k64_slot((wm * MBW + mb) * 16 + i16, g16) * 8]);
 #pragma unroll
-            for (int nb = 0; nb < NBW; ++nb) {
-                const int col = (wn * NBW + nb) * 16 + 4 * (i16 & 3);
-                const int row = s * BKG + 8 * g16 + (i16 >> 2);
-                const bf16x4_t lo = lds_tr(&wsb[row * WP + col]);
-                const bf16x4_t hi = lds_tr(&wsb[(row + 4) * WP + col]);
-                const bf16x8_t wf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            for (int s = 0; s < 3; ++s)
 #pragma unroll
-                for (int mb = 0; mb < MBW; ++mb)
-                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xf[mb], acc[mb][nb], 0, 0, 0);
-            }
+                for (int nb = 0; nb < NBW; ++nb)
+                    wf[q][s][nb] = *reinterpret_cast<const bf16x8_t*>(
+                        &sq[k64_slot(BM + s * EP2 + (wn * NBW + nb) * 16 + i16, g16) * 8]);
         }
-        if (kt + 1 < nk) store(cur ^ 1);
-        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < KS; ++q)
+#pragma unroll
+            for (int s = 0; s < 3; ++s)
+#pragma unroll
+                for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+                    for (int mb = 0; mb < MBW; ++mb)
+                        acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[q][s][nb], xf[q][mb], acc[mb][nb],
+                                                                               0, 0, 0);
+        slot = slot + 1 == NS ? 0 : slot + 1;
     }
+    // the trailing out-of-range loads still write the ring, which the logit
+    // tile overlays
+    dma_barrier<0>();
 
     // logits (+ bias) -> LDS tile [BM][EP2]
 #pragma unroll
@@ -236,7 +262,7 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(RouteArgs a, const uint
             if (t0 + tl < T) a.logits[(t0 + tl) * E + e] = sm.lt[tl * LTP + e];
         }
     }
-    constexpr int G = EP2 / 4 > 64 ? 64 : EP2 / 4;
+    constexpr int G = EP2 / 4 > 16 ? 16 : EP2 / 4;
     constexpr int NV = EP2 / G;
     constexpr int GPW = 64 / G;   // tokens per wave per pass
     const int gl = lane & (G - 1), gi = lane / G;
@@ -257,30 +283,39 @@ int route_mfma_ep2(int E) {
     return e;
 }
 
-// the top-k groups have EP2/4 lanes (at most 64) and lane j keeps the j-th pick
+// the top-k groups have EP2/4 lanes (at most 16) and lane j keeps the j-th pick
 bool route_mfma_supported(int dtype, int E, int k) {
     const int ep2 = route_mfma_ep2(E);
-    const int g = ep2 / 4 > 64 ? 64 : ep2 / 4;
+    const int g = ep2 / 4 > 16 ? 16 : ep2 / 4;
     return dtype == MOE_BF16 && E <= 256 && k <= g;
 }
 
 size_t route_mfma_ws_bytes(int d, int E) { return (size_t)3 * d * route_mfma_ep2(E) * sizeof(uint16_t); }
 
-template <int EP2, int BM>
+template <int EP2, int BM, int NS, int KS>
 static void launch_bm(const RouteArgs& a, const uint16_t* W3, hipStream_t st) {
     const dim3 grid((unsigned)((a.T + BM - 1) / BM));
-    hipLaunchKernelGGL((route_mfma_kernel<EP2, BM>), grid, dim3(256), 0, st, a, W3);
+    hipLaunchKernelGGL((route_mfma_kernel<EP2, BM, NS, KS>), grid, dim3(256), 0, st, a, W3);
 }
 
+// Tile choice per expert width.  Up to 128 experts: 32- or 64-token tiles,
+// two K-steps per stage (one barrier and one batch of LDS reads per 64 of
+// K), ring of 4 slots (3 of 52 KiB for 128 experts).  256 experts: 128-token tiles halve the re-reads
+// of the 3 MiB weight split per token; one K-step per stage, 2 slots.
 template <int EP2>
 static void launch_ep2(const RouteArgs& a, const uint16_t* W3, int cus, hipStream_t st) {
-    // 64-token tiles halve the weight traffic per token once they still fill the CUs
     constexpr int WM = 4 / (EP2 / 16 >= 4 ? 4 : EP2 / 16);
-    if constexpr (16 * WM > 32) {
-        launch_bm<EP2, 64>(a, W3, st);
+    if constexpr (EP2 == 256) {
+        if ((a.T + 127) / 128 >= cus) launch_bm<256, 128, 2, 1>(a, W3, st);
+        else launch_bm<256, 64, 3, 1>(a, W3, st);
+    } else if constexpr (EP2 == 128) {
+        launch_bm<128, 32, 3, 2>(a, W3, st);
+    } else if constexpr (16 * WM > 32) {
+        launch_bm<EP2, 64, 4, 2>(a, W3, st);
     } else {
-        if ((a.T + 63) / 64 >= 2 * cus) launch_bm<EP2, 64>(a, W3, st);
-        else launch_bm<EP2, 32>(a, W3, st);
+        // 64-token tiles halve the weight traffic per token once they still fill the CUs
+        if ((a.T + 63) / 64 >= cus) launch_bm<EP2, 64, 4, 2>(a, W3, st);
+        else launch_bm<EP2, 32, 4, 2>(a, W3, st);
     }
 }
 
