@@ -606,7 +606,7 @@ static bool try_pipe(const GemmArgs& g, int64_t max_rows, hipStream_t st, hipErr
 template <int EPI>
 static hipError_t launch_epi(const GemmArgs& g, int64_t max_rows, hipStream_t st) {
     hipError_t err = hipSuccess;
-    if (try_pipe<TilePipe, 4, 1024, 2, EPI>(g, max_rows, st, &err)) return err;
+    if (try_pipe<TilePipe, 4, 1024, TilePipe::NW >= 8 ? 2 : 1, EPI>(g, max_rows, st, &err)) return err;
     hipLaunchKernelGGL((ffn_gemm_bf16_kernel<TileSmall, EPI>), dim3(small_blocks<TileSmall, EPI>()),
                        dim3(TileSmall::NT), 0, st, g);
     return hipGetLastError();

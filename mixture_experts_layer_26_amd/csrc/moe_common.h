@@ -45,16 +45,19 @@ __device__ __forceinline__ float gelu_erf(float u) {
 // negative tail.  Used where h is rounded to bf16 (8 mantissa bits), far
 // coarser than this error.
 __device__ __forceinline__ float gelu_as(float u) {
-    const float z = fabsf(u) * 0.70710678118654752440f;
-    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
-    float poly = fmaf(t, 1.061405429f, -1.453152027f);
-    poly = fmaf(t, poly, 1.421413741f);
-    poly = fmaf(t, poly, -0.284496736f);
-    poly = fmaf(t, poly, 0.254829592f);
-    poly *= t;
-    const float e = __builtin_amdgcn_exp2f(-z * z * 1.44269504088896340736f);  // exp(-z^2)
-    const float q = 0.5f * poly * e;
-    return u * (u >= 0.0f ? 1.0f - q : q);
+    // t = 1 / (1 + p z) with z = |u| / sqrt 2; the polynomial carries the
+    // factor 1/2 of q; exp(-z^2) = exp2(-u^2 log2(e) / 2)
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f * 0.70710678118654752440f, fabsf(u), 1.0f));
+    float poly = fmaf(t, 0.5f * 1.061405429f, 0.5f * -1.453152027f);
+    poly = fmaf(t, poly, 0.5f * 1.421413741f);
+    poly = fmaf(t, poly, 0.5f * -0.284496736f);
+    poly = fmaf(t, poly, 0.5f * 0.254829592f);
+    const float e = __builtin_amdgcn_exp2f(u * (u * (-0.5f * 1.44269504088896340736f)));
+    const float q = poly * t * e;
+    // u (1 - q) for u >= 0 and u q for u < 0, as max(u, 0) - |u| q; |u| is
+    // clamped to the largest float so that u = +-inf gives +inf and 0
+    // (q = 0 there) and a NaN stays NaN
+    return fmaxf(u, 0.0f) - fminf(fabsf(u), 3.40282347e38f) * q;
 }
 
 template <typename T>
