@@ -39,8 +39,8 @@ STAGE_KERNELS = {
     "hist": ("hist_kernel",),
     "scatter": ("scatter_kernel",),
     "gather": ("gather_kernel",),
-    "ffn1": ("ffn_gemm_bf16_kernel<", ", 0>"),
-    "ffn2": ("ffn_gemm_bf16_kernel<", ", 1>"),
+    "ffn1": ("ffn_gemm_", ", 0>(moe::GemmArgs)"),
+    "ffn2": ("ffn_gemm_", ", 1>(moe::GemmArgs)"),
     "combine": ("combine_kernel",),
 }
 
