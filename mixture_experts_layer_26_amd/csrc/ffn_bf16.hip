@@ -340,28 +340,58 @@ __device__ __forceinline__ void mfma_half32(f32x16_t (&acc)[C::MB][C::NB], const
 }
 
 // accumulator [mb][nb] of lane l, elements 4q..4q+3: row 32 mb + l % 32,
-// columns 32 nb + 8 q + 4 (l / 32)..+3; bias from the item's LDS slice, one
-// quad live at a time
+// columns 32 nb + 8 q + 4 (l / 32)..+3; bias quads re-read from the item's
+// LDS slice.  Rows outermost: the stores that fill one row's 128-byte lines
+// issue back to back (row pieces spread over the epilogue measured up to
+// twice the HBM write bytes).
+// bf16 h: the two lanes of a row each hold 8-byte pieces; the upper half of
+// the wave trades its quad q for the lower half's quad q + 1 (q even), so each
+// lane stores 8 consecutive columns and a store covers 32 contiguous bytes
+// of a row.
 template <class C, int EPI>
 __device__ __forceinline__ void epilogue32(const GemmArgs& g, const Item<C>& it, const f32x16_t (&acc)[C::MB][C::NB],
                                            const float* sbias, int wm, int wn, int lane) {
+    const int h = lane >> 5;
 #pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb)
+    for (int mb = 0; mb < C::MB; ++mb) {
+        const int ml = wm * C::TM + mb * 32 + (lane & 31);
+        const bool row_ok = ml < it.mrows;
+        const int64_t row = it.m0 + ml;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int nl = wn * C::TN + nb * 32 + 8 * q + 4 * (lane >> 5);
-            const int n = it.n0 + nl;
-            if (n >= g.N) continue;
-            const f32x4_t b = *reinterpret_cast<const f32x4_t*>(&sbias[nl]);
+        for (int nb = 0; nb < C::NB; ++nb) {
+            if constexpr (EPI == EPI_GELU_H) {
 #pragma unroll
-            for (int mb = 0; mb < C::MB; ++mb) {
-                const int ml = wm * C::TM + mb * 32 + (lane & 31);
-                if (ml >= it.mrows) continue;
-                const f32x4_t v = {acc[mb][nb][4 * q], acc[mb][nb][4 * q + 1], acc[mb][nb][4 * q + 2],
-                                   acc[mb][nb][4 * q + 3]};
-                store4<EPI>(g, it.m0 + ml, n, v + b);
+                for (int q = 0; q < 4; q += 2) {
+                    const int nl = wn * C::TN + nb * 32 + 8 * q + 4 * h;
+                    const int n = it.n0 + wn * C::TN + nb * 32 + 8 * q + 8 * h;
+                    uint32_t p[2][2];
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const f32x4_t b = *reinterpret_cast<const f32x4_t*>(&sbias[nl + 8 * j]);
+                        const int e = 4 * (q + j);
+                        p[j][0] = pack_bf16x2(gelu_as(acc[mb][nb][e] + b[0]), gelu_as(acc[mb][nb][e + 1] + b[1]));
+                        p[j][1] = pack_bf16x2(gelu_as(acc[mb][nb][e + 2] + b[2]), gelu_as(acc[mb][nb][e + 3] + b[3]));
+                    }
+                    const auto x = __builtin_amdgcn_permlane32_swap(p[0][0], p[1][0], false, false);
+                    const auto y = __builtin_amdgcn_permlane32_swap(p[0][1], p[1][1], false, false);
+                    if (!row_ok || n >= g.N) continue;
+                    const uint4 o = {x[0], y[0], x[1], y[1]};
+                    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(g.out) + row * g.N + n) = o;
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int nl = wn * C::TN + nb * 32 + 8 * q + 4 * h;
+                    const int n = it.n0 + nl;
+                    if (!row_ok || n >= g.N) continue;
+                    const f32x4_t b = *reinterpret_cast<const f32x4_t*>(&sbias[nl]);
+                    const f32x4_t v = {acc[mb][nb][4 * q], acc[mb][nb][4 * q + 1], acc[mb][nb][4 * q + 2],
+                                       acc[mb][nb][4 * q + 3]};
+                    store4<EPI>(g, row, n, v + b);
+                }
             }
         }
+    }
 }
 
 }  // namespace
