@@ -50,6 +50,8 @@ def lib():
                                           _P, _P, _P, _P, _P, _P]
         L.oracle_aux.restype = C.c_double
         L.oracle_aux.argtypes = [_I64, _I64, _I64, _P, C.c_double]
+        L.oracle_coactivation.argtypes = [_I64, _I64, _I64, _P, _P, _P]
+        L.oracle_load_stats.argtypes = [_I64, _P, _P, _P, _P]
         L.oracle_layer_forward.argtypes = ([_I64] * 5 + [C.c_int, C.c_float, C.c_double, C.c_double]
                                            + [_P] * 18)
         _lib = L
@@ -148,6 +150,25 @@ def layer_tokens(toks, x, W1, b1, W2, b2, idx, slot, w) -> np.ndarray:
 def aux(counts, T: int, k: int, lam: float) -> float:
     counts = _c(counts, np.int32)
     return float(lib().oracle_aux(len(counts), T, k, _p(counts), float(lam)))
+
+
+def coactivation(idx, E: int):
+    """Ordered co-selection counts H [E, E] int64 (H[i, j]: tokens that list
+    expert i before expert j) and per-expert loads routed [E] int64."""
+    idx = _c(idx, np.int32)
+    T, k = idx.shape
+    H = np.empty((E, E), np.int64)
+    routed = np.empty(E, np.int64)
+    lib().oracle_coactivation(T, E, k, _p(idx), _p(H), _p(routed))
+    return H, routed
+
+
+def load_stats(load) -> dict:
+    """mean, population variance and CV of per-expert loads (float64)."""
+    load = _c(load, np.int64)
+    m, v, c = C.c_double(), C.c_double(), C.c_double()
+    lib().oracle_load_stats(len(load), _p(load), C.byref(m), C.byref(v), C.byref(c))
+    return dict(mean=m.value, var=v.value, cv=c.value)
 
 
 def layer_forward(x, Wg, bg, W1, b1, W2, b2, k: int, cf: float = 0.0, tau: float = 1.0,

@@ -294,6 +294,41 @@ double oracle_aux(int64_t E, int64_t T, int64_t k, const int32_t* counts, double
     return lam * s;
 }
 
+/* Routing heat map, [EP] section 3.2 step 1: for every token, every pair of
+ * its chosen experts adds one to H[i][j], where i is the expert at the
+ * earlier position of the token's top-k list and j the one at the later
+ * position.  The page notes the matrix is not symmetric; reading it as these
+ * ordered pairs, H + H^T counts the tokens that chose both experts.
+ * routed[e] counts every slot (t, j) that chose e ([EP] section 2.1, the
+ * per-expert load). */
+void oracle_coactivation(int64_t T, int64_t E, int64_t k, const int32_t* idx, int64_t* H,
+                         int64_t* routed) {
+    for (int64_t i = 0; i < E * E; ++i) H[i] = 0;
+    for (int64_t e = 0; e < E; ++e) routed[e] = 0;
+    for (int64_t t = 0; t < T; ++t) {
+        const int32_t* row = idx + t * k;
+        for (int64_t a = 0; a < k; ++a) {
+            routed[row[a]] += 1;
+            for (int64_t b = a + 1; b < k; ++b) H[(int64_t)row[a] * E + row[b]] += 1;
+        }
+    }
+}
+
+/* Load statistics of the per-expert loads: mean, population variance (the
+ * balance loss of [PyTorchMoE] section 3.3 item 1: the mean squared
+ * deviation of the loads from their mean) and coefficient of variation
+ * std / mean ([EP] section 2.1). */
+void oracle_load_stats(int64_t E, const int64_t* load, double* mean, double* var, double* cv) {
+    double s = 0.0;
+    for (int64_t e = 0; e < E; ++e) s += (double)load[e];
+    double m = s / (double)E;
+    double q = 0.0;
+    for (int64_t e = 0; e < E; ++e) q += ((double)load[e] - m) * ((double)load[e] - m);
+    *mean = m;
+    *var = q / (double)E;
+    *cv = m > 0.0 ? sqrt(*var) / m : 0.0;
+}
+
 /* Whole layer, oracle-only mode: the routing uses the oracle's own logits
  * rounded to float32 (the precision the routing decision is taken in). */
 void oracle_layer_forward(int64_t T, int64_t d, int64_t E, int64_t k, int64_t dff,

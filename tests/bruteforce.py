@@ -48,3 +48,19 @@ def dispatch(idx: Sequence[Sequence[int]], E: int, cap: int):
             perm[row] = t
             slot[t][j] = row
     return dict(routed=routed, counts=counts, offsets=offsets, perm=perm, slot=slot)
+
+
+def coactivation(idx: Sequence[Sequence[int]], E: int):
+    """H[i][j] = number of tokens whose list holds both i and j with i at the
+    earlier position, found by looking both experts up in every list."""
+    H = [[0] * E for _ in range(E)]
+    for i in range(E):
+        for j in range(E):
+            n = 0
+            for row in idx:
+                row = list(row)
+                if i in row and j in row and row.index(i) < row.index(j):
+                    n += 1
+            H[i][j] = n
+    routed = [sum(list(row).count(e) for row in idx) for e in range(E)]
+    return H, routed

@@ -314,3 +314,66 @@ def test_layer_forward_equals_its_parts(orc):
         assert np.array_equal(dsp[key], out[key])
     assert np.array_equal(y, out["y"])
     assert (dsp["slot"] < 0).any(), "this case is meant to drop slots"
+
+
+# ---- routing heat map and load telemetry ([EP] 3.2 step 1, 2.1; [PyTorchMoE] 3.3) ----
+
+def _distinct_rows(rng, T, E, k):
+    return np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("seed,T,E,k", [(0, 40, 6, 3), (1, 25, 5, 5), (2, 30, 7, 1), (3, 60, 4, 2)])
+def test_coactivation_bruteforce(orc, seed, T, E, k):
+    idx = _distinct_rows(_rng(seed), T, E, k)
+    H, routed = orc.coactivation(idx, E)
+    Hb, rb = bf.coactivation(idx.tolist(), E)
+    assert H.tolist() == Hb
+    assert routed.tolist() == rb
+
+
+def test_coactivation_invariants(orc):
+    rng = _rng(7)
+    T, E, k = 500, 16, 4
+    idx = _distinct_rows(rng, T, E, k)
+    H, routed = orc.coactivation(idx, E)
+    assert H.sum() == T * k * (k - 1) // 2
+    assert np.all(np.diag(H) == 0)
+    assert routed.sum() == T * k
+    # every token that chose e pairs it with its k - 1 other experts
+    assert np.array_equal((H + H.T).sum(axis=1), routed * (k - 1))
+
+
+def test_coactivation_order_closed_forms(orc):
+    T, E = 33, 5
+    H, routed = orc.coactivation(np.tile(np.array([[0, 1]], np.int32), (T, 1)), E)
+    ref = np.zeros((E, E), np.int64)
+    ref[0, 1] = T
+    assert np.array_equal(H, ref)
+    H2, _ = orc.coactivation(np.tile(np.array([[1, 0]], np.int32), (T, 1)), E)
+    assert np.array_equal(H2, ref.T)
+    assert routed.tolist() == [T, T, 0, 0, 0]
+    # k = E: every token chose every expert, so H + H^T = T (J - I)
+    idx = _distinct_rows(_rng(3), T, E, E)
+    H3, r3 = orc.coactivation(idx, E)
+    assert np.array_equal(H3 + H3.T, T * (np.ones((E, E), np.int64) - np.eye(E, dtype=np.int64)))
+    assert np.all(r3 == T)
+    # k = 1: no pairs
+    H4, _ = orc.coactivation(idx[:, :1], E)
+    assert not H4.any()
+
+
+def test_load_stats_closed_forms(orc):
+    import statistics
+    E, T = 8, 1000
+    s = orc.load_stats(np.full(E, 250, np.int64))
+    assert s["mean"] == 250 and s["var"] == 0 and s["cv"] == 0
+    one = np.zeros(E, np.int64)
+    one[0] = T   # k = 1, every token on expert 0
+    s = orc.load_stats(one)
+    assert math.isclose(s["var"], T * T * (E - 1) / E ** 2, rel_tol=1e-15)
+    assert math.isclose(s["cv"], math.sqrt(E - 1), rel_tol=1e-15)
+    load = _rng(5).integers(0, 900, 64).astype(np.int64)
+    s = orc.load_stats(load)
+    assert math.isclose(s["var"], statistics.pvariance(load.tolist()), rel_tol=1e-12)
+    assert math.isclose(s["cv"], statistics.pstdev(load.tolist()) / statistics.fmean(load.tolist()),
+                        rel_tol=1e-12)
