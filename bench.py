@@ -194,6 +194,36 @@ def load_traffic(workload: str, stage: str):
     return rec.get("bytes_per_launch")
 
 
+def time_heat_map(moe, s, cfg, d, y, counts, aux, ws, stream, reps=20):
+    """Routing heat map + load telemetry (moe_coactivation) on the top-k
+    lists of one layer forward of the same workload; HIP events around each
+    call on the call's stream.  Algorithmic bytes: read T*k indices, write
+    the E x E counts and the E loads."""
+    import numpy as np
+    import torch
+    dev = y.device
+    idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev)
+    moe.moe_layer_forward(s, d["x"], d["Wg"], d["bg"], d["W1"], d["b1"], d["W2"], d["b2"], y,
+                          counts, aux, ws, topk_idx=idx, stream=stream)
+    Hm = torch.empty((cfg.E, cfg.E), dtype=torch.int32, device=dev)
+    rt = torch.empty(cfg.E, dtype=torch.int32, device=dev)
+    st = torch.empty(3, dtype=torch.float32, device=dev)
+    for _ in range(3):
+        moe.moe_coactivation(s, idx, Hm, rt, st, stream=stream)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record(stream)
+        moe.moe_coactivation(s, idx, Hm, rt, st, stream=stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = 1e3 * float(np.median([a.elapsed_time(b) for a, b in ev]))
+    nbytes = cfg.T * cfg.k * 4 + cfg.E * cfg.E * 4 + cfg.E * 4
+    stats = st.cpu().numpy()
+    return {"us": us, "algorithmic_bytes": nbytes, "GB/s": nbytes / (us * 1e-6) / 1e9,
+            "frac_hbm": nbytes / (us * 1e-6) / PEAK_HBM, "pairs": cfg.T * cfg.k * (cfg.k - 1) // 2,
+            "load_mean": float(stats[0]), "load_var": float(stats[1]), "load_cv": float(stats[2])}
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -317,6 +347,7 @@ def main():
         "aux": float(aux.cpu().numpy()[0]),
         "setup_seconds": round(t_gen, 2),
     }
+    out["heat_map"] = time_heat_map(moe, s, cfg, d, y, counts, aux, ws, stream)
     if args.copy_calib:
         src = torch.empty(COPY_CALIB_BYTES, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

@@ -182,6 +182,24 @@ int moe_combine(const moe_shape* s, const float* out_perm, const int32_t* slot,
  *    kept counts ([EP] 2.3, taken as printed). */
 int moe_aux_loss(const moe_shape* s, const int32_t* counts, float* aux, void* stream);
 
+/* 6. Routing heat map and load telemetry, from topk_idx [T,k] (as written by
+ *    moe_route).  [EP] section 3.2 step 1: the experts' co-selection counts
+ *    per batch, the input of affinity-aware expert placement; the page calls
+ *    the matrix non-symmetric, read here as ordered pairs:
+ *      H[i*E + j] = number of tokens t with topk_idx[t,a] = i and
+ *                   topk_idx[t,b] = j for some a < b
+ *    (i ranked above j; H + H^T counts the tokens that chose both experts;
+ *    the diagonal is 0 for distinct experts).  routed[e] = number of slots
+ *    (t, j) with topk_idx[t,j] = e, before capacity ([EP] section 2.1, the
+ *    per-expert load).  stats (NULL ok) = {mean load, population variance
+ *    of the loads ([PyTorchMoE] section 3.3 item 1), coefficient of
+ *    variation std / mean ([EP] section 2.1)}, computed in fp64 and stored
+ *    as fp32.  H (int32 [E,E]) and routed (int32 [E]) are overwritten.
+ *    Indices outside [0, E) are skipped (in-bounds, not counted).  Counts
+ *    are exact integers, independent of the order of the atomic updates. */
+int moe_coactivation(const moe_shape* s, const int32_t* topk_idx, int32_t* H, int32_t* routed,
+                     float* stats /* NULL ok, [3] */, void* stream);
+
 /* The whole layer in one call: steps 1-5 on one stream (the balance loss is
  * produced by the dispatch step).  Writes y, counts and aux; routed,
  * topk_idx, topk_w and logits are optional outputs (NULL ok).  perm, slot,

@@ -1,6 +1,7 @@
 """Build libmoe.so (HIP, gfx950) in-tree.
 
-    python -m mixture_experts_layer_26_amd.build
+    python mixture_experts_layer_26_amd/build.py   (by path: importing the
+    package would load the previous library)
 
 Every csrc/*.hip file is compiled with hipcc for gfx950 into _build/, then
 linked into mixture_experts_layer_26_amd/libmoe.so.  Packed fp32 VALU

@@ -329,6 +329,16 @@ __device__ __forceinline__ void read_frags32(Frags32<C>& f, const uint16_t* as, 
         }
 }
 
+// scheduling groups: one MFMA, then R LDS reads, N times
+template <int N, int R>
+__device__ __forceinline__ void interleave_mfma_reads() {
+    if constexpr (N > 0) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+        interleave_mfma_reads<N - 1, R>();
+    }
+}
+
 // the MFMAs of K-half h of one step
 template <class C>
 __device__ __forceinline__ void mfma_half32(f32x16_t (&acc)[C::MB][C::NB], const Frags32<C>& f, int h) {
@@ -552,17 +562,20 @@ __global__ __launch_bounds__(C::NT, WPE) void ffn_gemm_bf16_pipe_kernel(GemmArgs
     int c_slot = 0, c_bslot = 0;
     int64_t item = range.first;
     f32x16_t acc[C::MB][C::NB];
+    constexpr int kReadsPerMfma = (4 * C::NB + 2 * C::MB) / (C::MB * C::NB);
+    static_assert(kReadsPerMfma * C::MB * C::NB == 4 * C::NB + 2 * C::MB, "reads split evenly over MFMAs");
     auto step = [&](Frags32<C>& cur, Frags32<C>& nxt) {
         pipe_barrier<(NS - 2) * PER>();
         const int ns = c_slot + 1 == NS ? 0 : c_slot + 1;
-        // all next-step reads first (they return while the MFMAs run), then the
-        // first K-half of MFMAs, then this step's global -> LDS loads, then the
-        // second K-half: the loads of eight waves take the TA ~500 cycles per
-        // step, and issued right after the barrier they held back the MFMAs
+        // the next step's fragment reads interleaved with the first K-half of
+        // MFMAs (one MFMA, then two reads: a wave whose reads all came first
+        // waited on the LDS queue before its first MFMA), then this step's
+        // global -> LDS loads, then the second K-half: the loads of eight waves
+        // take the TA ~500 cycles per step, and issued right after the barrier
+        // they held back the MFMAs
         read_frags32<C>(nxt, sa[ns], sb[ns], wm, wn, lane);
         mfma_half32<C>(acc, cur, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 4 * C::NB + 2 * C::MB, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, C::MB * C::NB, 0);
+        interleave_mfma_reads<C::MB * C::NB, kReadsPerMfma>();
         __builtin_amdgcn_sched_barrier(0);
         issue_next();
         __builtin_amdgcn_sched_barrier(0);

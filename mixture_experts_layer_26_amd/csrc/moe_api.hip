@@ -390,6 +390,20 @@ int moe_aux_loss(const moe_shape* s, const int32_t* counts, float* aux, void* st
     return MOE_OK;
 }
 
+int moe_coactivation(const moe_shape* s, const int32_t* topk_idx, int32_t* H, int32_t* routed, float* stats,
+                     void* stream) {
+    Geo g;
+    if (int rc = validate(s, &g)) return rc;
+    MOE_REQUIRE(topk_idx);
+    MOE_REQUIRE(H);
+    MOE_REQUIRE(routed);
+    MOE_OPTIONAL(stats);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    MOE_HIP(launch_coactivation(g.T, (int)g.k, (int)g.E, topk_idx, H, routed, stats, device_cu_count(), st),
+            "coactivation kernel launch");
+    return MOE_OK;
+}
+
 int moe_layer_forward(const moe_shape* s, const void* x, const float* Wg, const float* bg, const void* W1,
                       const float* b1, const void* W2, const float* b2, float* y, int32_t* counts,
                       float* aux, int32_t* routed, int32_t* topk_idx, float* topk_w, float* logits,

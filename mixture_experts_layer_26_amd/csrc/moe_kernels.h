@@ -75,6 +75,10 @@ hipError_t launch_combine(int64_t T, int d, int k, const float* out_perm, const 
 hipError_t launch_aux(int E, int64_t T, int k, float lambda, const int32_t* counts, float* aux,
                       hipStream_t st);
 
+// ---- coact.hip: routing heat map and load telemetry -----------------------
+hipError_t launch_coactivation(int64_t T, int k, int E, const int32_t* idx, int32_t* H, int32_t* routed,
+                               float* stats, int cus, hipStream_t st);
+
 // device properties (moe_api.hip)
 int device_cu_count();
 

@@ -1,0 +1,146 @@
+"""GPU parity of the routing heat map and load telemetry (moe_coactivation)
+against the oracle: H and routed must be identical integers, the load
+statistics within 1e-6 relative (fp64 on both sides, stored as fp32).
+
+Inputs are top-k lists with the structure of the workloads: Zipf-skewed
+expert popularity (the 64-expert skewed workload), a share of clustered
+tokens that all choose the same experts (the 256-expert workload's hot
+pairs), k from 1 to 32, E on both sides of the LDS / global-atomic switch at
+256, and the ragged token counts of several workgroups."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import gpu_harness as H
+
+pytestmark = pytest.mark.gpu
+
+TOL_STATS = 1e-6
+
+
+@pytest.fixture(scope="module")
+def moe():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    import mixture_experts_layer_26_amd as m
+    return m
+
+
+def topk_lists(T, E, k, seed, zipf_s=1.2, alpha=0.24, hot_frac=0.3, n_hot=16):
+    """Distinct experts per token: Zipf(zipf_s)-tilted popularity with
+    exponent alpha (scores = alpha * log p + Gumbel noise, top-k of them), and
+    a hot_frac share of tokens copying one of n_hot fixed lists."""
+    r = np.random.default_rng(seed)
+    logp = -zipf_s * np.log(np.arange(1, E + 1))
+    scores = alpha * logp[None, :] + r.gumbel(size=(T, E))
+    idx = np.argsort(-scores, axis=1, kind="stable")[:, :k].astype(np.int32)
+    if hot_frac > 0 and T > 1:
+        hot = np.stack([r.permutation(E)[:k] for _ in range(n_hot)]).astype(np.int32)
+        rows = r.random(T) < hot_frac
+        idx[rows] = hot[r.integers(0, n_hot, int(rows.sum()))]
+    return np.ascontiguousarray(idx)
+
+
+def run(moe, idx, E, stats=True):
+    import torch
+    T, k = idx.shape
+    s = moe.shape(T, 64, E, k, 64)
+    Hm = H.empty((E, E), torch.int32)
+    routed = H.empty(E, torch.int32)
+    st = H.empty(3, torch.float32) if stats else None
+    Hm.fill_(-7)
+    routed.fill_(-7)
+    moe.moe_coactivation(s, H.to_dev(idx), Hm, routed, st)
+    torch.cuda.synchronize()
+    return H.to_host(Hm), H.to_host(routed), (H.to_host(st) if stats else None)
+
+
+def check(moe, orc, idx, E):
+    Hg, rg, sg = run(moe, idx, E)
+    Hr, rr = orc.coactivation(idx, E)
+    assert np.array_equal(Hg.astype(np.int64), Hr), "H differs"
+    assert np.array_equal(rg.astype(np.int64), rr), "routed differs"
+    ref = orc.load_stats(rr)
+    for i, key in enumerate(("mean", "var", "cv")):
+        want = ref[key]
+        assert abs(float(sg[i]) - want) <= TOL_STATS * max(abs(want), 1e-30), (key, float(sg[i]), want)
+
+
+@pytest.mark.parametrize("T,E,k", [
+    (8192, 64, 2),        # the 64-expert skewed workload's shape
+    (8192, 128, 8),       # hybrid: 128 experts, top-8
+    (32768, 256, 2),      # 256 experts, clustered tokens
+    (4096, 16, 2),
+    (256, 8, 2),
+    (1000, 257, 3),       # first E on global atomics
+    (3001, 1000, 5),
+    (777, 1024, 32),      # largest E and k
+    (70001, 200, 4),      # many workgroups, ragged tail
+])
+def test_coactivation_parity(moe, orc, T, E, k):
+    H.log(f"[coact] T={T} E={E} k={k}")
+    check(moe, orc, topk_lists(T, E, k, seed=T + E + k), E)
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 8, 2), (1, 1, 1), (5, 8, 8), (300, 4, 1), (64, 2, 2)])
+def test_coactivation_edge_cases(moe, orc, T, E, k):
+    H.log(f"[coact-edge] T={T} E={E} k={k}")
+    r = np.random.default_rng(T * 31 + E)
+    idx = np.stack([r.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    check(moe, orc, idx, E)
+
+
+def test_coactivation_route_output(moe, orc):
+    """The heat map of the lists the gate itself produced (medium bf16 layer)."""
+    import torch
+    from moe_inputs import get, make_inputs
+    cfg = get("medium_bf16")
+    inp = make_inputs(cfg)
+    s = H.make_shape(moe, cfg)
+    idx = H.empty((cfg.T, cfg.k), torch.int32)
+    w = H.empty((cfg.T, cfg.k), torch.float32)
+    moe.moe_route(s, H.to_dev(inp["x"]), H.to_dev(inp["Wg"]), H.to_dev(inp["bg"]), None, idx, w,
+                  moe.workspace(s))
+    torch.cuda.synchronize()
+    check(moe, orc, H.to_host(idx), cfg.E)
+
+
+def test_coactivation_counter_limit(moe, orc):
+    """Every token on the same ordered pair, with enough tokens that each
+    workgroup counts the 16-bit maximum of 65535 for that pair."""
+    E, T = 16, 256 * 65535 + 1000
+    H.log(f"[coact-limit] T={T}")
+    idx = np.tile(np.array([[3, 5]], np.int32), (T, 1))
+    Hg, rg, sg = run(moe, idx, E)
+    ref = np.zeros((E, E), np.int64)
+    ref[3, 5] = T
+    assert np.array_equal(Hg.astype(np.int64), ref)
+    assert rg.tolist() == [T if e in (3, 5) else 0 for e in range(E)]
+
+
+def test_coactivation_skips_out_of_range(moe):
+    """Indices outside [0, E) count nothing; the valid pairs of the same
+    token still count (expected values by direct enumeration)."""
+    E = 6
+    idx = np.array([[0, 1, 2], [-1, 2, 3], [4, E, 5], [E + 100, -5, 1], [5, 4, 3]], np.int32)
+    Hg, rg, _ = run(moe, idx, E, stats=False)
+    ref = np.zeros((E, E), np.int64)
+    rr = np.zeros(E, np.int64)
+    for row in idx.tolist():
+        for a in range(3):
+            if not 0 <= row[a] < E:
+                continue
+            rr[row[a]] += 1
+            for b in range(a + 1, 3):
+                if 0 <= row[b] < E:
+                    ref[row[a], row[b]] += 1
+    assert np.array_equal(Hg.astype(np.int64), ref)
+    assert np.array_equal(rg.astype(np.int64), rr)
+
+
+def test_coactivation_repeatable(moe):
+    idx = topk_lists(20000, 256, 2, seed=3)
+    a = run(moe, idx, 256)
+    b = run(moe, idx, 256)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and np.array_equal(a[2], b[2])
