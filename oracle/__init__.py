@@ -51,6 +51,10 @@ def lib():
         L.oracle_aux.restype = C.c_double
         L.oracle_aux.argtypes = [_I64, _I64, _I64, _P, C.c_double]
         L.oracle_coactivation.argtypes = [_I64, _I64, _I64, _P, _P, _P]
+        L.oracle_noisy_logits.argtypes = [_I64, _P, _P, C.c_float, _P]
+        L.oracle_route_top1_full.argtypes = [_I64, _I64, C.c_double, _P, _P, _P]
+        L.oracle_aux_variance.restype = C.c_double
+        L.oracle_aux_variance.argtypes = [_I64, _P, C.c_double]
         L.oracle_load_stats.argtypes = [_I64, _P, _P, _P, _P]
         L.oracle_layer_forward.argtypes = ([_I64] * 5 + [C.c_int, C.c_float, C.c_double, C.c_double]
                                            + [_P] * 18)
@@ -169,6 +173,31 @@ def load_stats(load) -> dict:
     m, v, c = C.c_double(), C.c_double(), C.c_double()
     lib().oracle_load_stats(len(load), _p(load), C.byref(m), C.byref(v), C.byref(c))
     return dict(mean=m.value, var=v.value, cv=c.value)
+
+
+def noisy_logits(L, noise, scale: float) -> np.ndarray:
+    """fp32(L + fp32(scale * noise)), scale taken as float32 (the stable
+    layer's exploration noise, in the page's fp32 arithmetic)."""
+    L, noise = _c(L, np.float32), _c(noise, np.float32)
+    out = np.empty(L.shape, np.float32)
+    lib().oracle_noisy_logits(L.size, _p(L), _p(noise), float(np.float32(scale)), _p(out))
+    return out
+
+
+def route_top1_full(logits32, tau: float = 1.0):
+    """Top-1 over all E with the full-softmax probability as weight:
+    (idx [T,1] int32, w [T,1] float64)."""
+    L = _c(logits32, np.float32)
+    T, E = L.shape
+    idx = np.empty((T, 1), np.int32)
+    w = np.empty((T, 1), np.float64)
+    lib().oracle_route_top1_full(T, E, float(tau), _p(L), _p(idx), _p(w))
+    return idx, w
+
+
+def aux_variance(load, lam: float) -> float:
+    load = _c(load, np.int64)
+    return float(lib().oracle_aux_variance(len(load), _p(load), float(lam)))
 
 
 def layer_forward(x, Wg, bg, W1, b1, W2, b2, k: int, cf: float = 0.0, tau: float = 1.0,

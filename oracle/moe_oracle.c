@@ -131,6 +131,49 @@ void oracle_route(int64_t T, int64_t E, int64_t k, double tau, const float* L,
     }
 }
 
+void oracle_load_stats(int64_t E, const int64_t* load, double* mean, double* var, double* cv);
+
+/* Exploration noise of the stable layer in [PyTorchMoE] section 4.3: during
+ * training the gate logits get scale * (standard normal draw) added before
+ * routing (scale 0.1 on the page).  The draws are an input.  The page does
+ * this in fp32, product first, then the sum, each rounded to fp32; the
+ * routing decision is taken on that fp32 value.  Here each step is exact in
+ * double (a product of two floats has 48 significant bits; a sum of two
+ * floats that does not fit 53 bits is dominated by its larger term) and is
+ * then rounded once to float. */
+void oracle_noisy_logits(int64_t n, const float* L, const float* noise, float scale, float* out) {
+    for (int64_t i = 0; i < n; ++i) {
+        float p = (float)((double)scale * (double)noise[i]);
+        out[i] = (float)((double)L[i] + (double)p);
+    }
+}
+
+/* Top-1 router of [PyTorchMoE] sections 2.3 and 4.3: a softmax over all E
+ * logits (divided by tau), the expert of the largest probability (ties to the
+ * lower index, as for top-k), and that probability as its weight.
+ * L are the fp32 logits under test; w in double. */
+void oracle_route_top1_full(int64_t T, int64_t E, double tau, const float* L, int32_t* idx, double* w) {
+    for (int64_t t = 0; t < T; ++t) {
+        const float* row = L + t * E;
+        int64_t best = 0;
+        for (int64_t e = 1; e < E; ++e)
+            if (row[e] > row[best]) best = e;   /* strict: equal values keep the lower index */
+        double z = 0.0;
+        for (int64_t e = 0; e < E; ++e) z += exp(((double)row[e] - (double)row[best]) / tau);
+        idx[t] = (int32_t)best;
+        w[t] = 1.0 / z;
+    }
+}
+
+/* Load-variance balance loss of [PyTorchMoE] section 3.3 item 1 (used with
+ * weight 0.01 by the stable layer of section 4.3): lambda times the mean
+ * squared deviation of the per-expert loads from their mean. */
+double oracle_aux_variance(int64_t E, const int64_t* load, double lam) {
+    double m, v, c;
+    oracle_load_stats(E, load, &m, &v, &c);
+    return lam * v;
+}
+
 /* Per-expert capacity.  [PithTrain] section 4.3 item 1 defines the capacity
  * as a factor times the per-expert share of the batch; with k slots per token
  * the share is T*k/E.  cap = min(T, ceil(cf*T*k/E)); cf <= 0 means no limit.

@@ -377,3 +377,64 @@ def test_load_stats_closed_forms(orc):
     assert math.isclose(s["var"], statistics.pvariance(load.tolist()), rel_tol=1e-12)
     assert math.isclose(s["cv"], statistics.pstdev(load.tolist()) / statistics.fmean(load.tolist()),
                         rel_tol=1e-12)
+
+
+# ---- router variants ([PyTorchMoE] 2.3, 3.3 item 1, 4.3) ----
+
+@pytest.mark.parametrize("seed,T,E,tau", [(0, 30, 5, 1.0), (1, 20, 16, 0.2), (2, 25, 3, 2.5)])
+def test_top1_full_softmax_matches_library(orc, seed, T, E, tau):
+    from scipy.special import softmax
+    r = _rng(seed)
+    L = r.integers(-4, 5, (T, E)).astype(np.float32)          # ties
+    L[::3] = r.standard_normal((len(L[::3]), E)).astype(np.float32)
+    idx, w = orc.route_top1_full(L, tau)
+    for t in range(T):
+        row = L[t].astype(np.float64)
+        best = max(range(E), key=lambda e: (row[e], -e))       # largest, then lowest index
+        assert idx[t, 0] == best
+        assert math.isclose(w[t, 0], softmax(row / tau)[best], rel_tol=1e-12)
+
+
+def test_top1_full_softmax_closed_forms(orc):
+    E = 6
+    L = np.zeros((3, E), np.float32)
+    L[1, 4] = np.float32(math.log(3.0))      # tau = 1: weight 3 / (3 + E - 1)
+    L[2] = -0.0
+    L[2, 3] = 0.0                            # -0 == +0: index 0 wins
+    idx, w = orc.route_top1_full(L, 1.0)
+    assert idx[:, 0].tolist() == [0, 4, 0]
+    assert math.isclose(w[0, 0], 1.0 / E, rel_tol=1e-15)
+    assert math.isclose(w[1, 0], 3.0 / (E + 2), rel_tol=1e-7)   # log 3 rounded to fp32
+    assert math.isclose(w[2, 0], 1.0 / E, rel_tol=1e-15)
+    # top-1 of the full softmax picks what top-k with k = 1 picks
+    L = _rng(9).standard_normal((200, 11)).astype(np.float32)
+    idx1, _ = orc.route_top1_full(L, 0.5)
+    idxk, wk = orc.route(L, 1, 0.5)
+    assert np.array_equal(idx1, idxk) and np.all(wk == 1.0)
+
+
+def test_noisy_logits_fp32_steps(orc):
+    """Each fp32 step rounded once from its exact rational value."""
+    from fractions import Fraction
+    r = _rng(4)
+    L = (r.standard_normal(300) * np.exp2(r.integers(-30, 30, 300))).astype(np.float32)
+    n = r.standard_normal(300).astype(np.float32)
+    out = orc.noisy_logits(L, n, 0.1)
+    s32 = Fraction(float(np.float32(0.1)))
+    for i in range(300):
+        p = np.float32(float(s32 * Fraction(float(n[i]))))
+        want = np.float32(float(Fraction(float(L[i])) + Fraction(float(p))))
+        assert out[i] == want, i
+    assert np.array_equal(orc.noisy_logits(L, n, 0.0), L)
+    assert np.array_equal(orc.noisy_logits(L, np.zeros_like(n), 0.1), L)
+
+
+def test_aux_variance_closed_forms(orc):
+    import statistics
+    E, T, lam = 8, 1000, 0.01
+    one = np.zeros(E, np.int64)
+    one[2] = T
+    assert math.isclose(orc.aux_variance(one, lam), lam * T * T * (E - 1) / E ** 2, rel_tol=1e-15)
+    assert orc.aux_variance(np.full(E, 7, np.int64), lam) == 0.0
+    load = _rng(6).integers(0, 500, 33).astype(np.int64)
+    assert math.isclose(orc.aux_variance(load, 0.5), 0.5 * statistics.pvariance(load.tolist()), rel_tol=1e-12)
