@@ -224,6 +224,52 @@ def time_heat_map(moe, s, cfg, d, y, counts, aux, ws, stream, reps=20):
             "load_mean": float(stats[0]), "load_var": float(stats[1]), "load_cv": float(stats[2])}
 
 
+def _median_us(fn, stream, reps=20):
+    import numpy as np
+    import torch
+    for _ in range(3):
+        fn()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return 1e3 * float(np.median([a.elapsed_time(b) for a, b in ev]))
+
+
+def time_router_variant(moe, s, cfg, d, ws, stream):
+    """The stable layer's router on the workload's gate logits: noisy top-1
+    over the full softmax (moe_route_logits_ex, writing the noisy logits)
+    and the load-variance loss (moe_aux_loss_ex).  Algorithmic bytes of the
+    router: read logits and noise, write the noisy logits, index and weight."""
+    import numpy as np
+    import torch
+    dev = d["x"].device
+    T, E = cfg.T, cfg.E
+    logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    i0 = torch.empty((T, cfg.k), dtype=torch.int32, device=dev)
+    w0 = torch.empty((T, cfg.k), dtype=torch.float32, device=dev)
+    moe.moe_route(s, d["x"], d["Wg"], d["bg"], logits, i0, w0, ws, stream=stream)
+    noise = torch.from_numpy(np.random.default_rng(11).standard_normal((T, E)).astype(np.float32)).to(dev)
+    s1 = moe.shape(T, cfg.d, E, 1, cfg.d_ff, 0.0, 1.0, 0.01)
+    idx = torch.empty((T, 1), dtype=torch.int32, device=dev)
+    w = torch.empty((T, 1), dtype=torch.float32, device=dev)
+    noisy = torch.empty((T, E), dtype=torch.float32, device=dev)
+    us_route = _median_us(lambda: moe.moe_route_logits_ex(s1, moe.MOE_ROUTER_TOP1_FULL, logits, idx, w, noise=noise,
+                                                          noise_scale=0.1, noisy_logits=noisy, stream=stream), stream)
+    routed = torch.empty(E, dtype=torch.int32, device=dev)
+    Hm = torch.empty((E, E), dtype=torch.int32, device=dev)
+    moe.moe_coactivation(s1, idx, Hm, routed, stream=stream)
+    aux = torch.empty(1, dtype=torch.float32, device=dev)
+    us_loss = _median_us(lambda: moe.moe_aux_loss_ex(s1, moe.MOE_LOSS_VARIANCE, routed, aux, stream=stream), stream)
+    nbytes = 3 * T * E * 4 + 8 * T
+    return {"top1_noisy_us": us_route, "top1_noisy_bytes": nbytes,
+            "top1_noisy_GB/s": nbytes / (us_route * 1e-6) / 1e9,
+            "top1_noisy_frac_hbm": nbytes / (us_route * 1e-6) / PEAK_HBM,
+            "variance_loss_us": us_loss, "variance_loss": float(aux.cpu().numpy()[0])}
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -348,6 +394,7 @@ def main():
         "setup_seconds": round(t_gen, 2),
     }
     out["heat_map"] = time_heat_map(moe, s, cfg, d, y, counts, aux, ws, stream)
+    out["router_variant"] = time_router_variant(moe, s, cfg, d, ws, stream)
     if args.copy_calib:
         src = torch.empty(COPY_CALIB_BYTES, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

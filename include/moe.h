@@ -182,6 +182,36 @@ int moe_combine(const moe_shape* s, const float* out_perm, const int32_t* slot,
  *    kept counts ([EP] 2.3, taken as printed). */
 int moe_aux_loss(const moe_shape* s, const int32_t* counts, float* aux, void* stream);
 
+/* 1c. Router variants of [PyTorchMoE] on fp32 logits [T,E] (e.g. the logits
+ *     moe_route wrote):
+ *     mode MOE_ROUTER_TOPK: as moe_route_logits (top-k, softmax over the k
+ *       selected logits divided by temperature);
+ *     mode MOE_ROUTER_TOP1_FULL (k must be 1; sections 2.3 and 4.3): the
+ *       expert of the largest logit (ties to the lower index) with, as its
+ *       weight, its probability under a softmax over all E logits divided by
+ *       temperature.
+ *     noise (NULL ok, [T,E] fp32): the training-time exploration noise of the
+ *       stable layer (section 4.3): the routed values are
+ *       fp32(L + fp32(noise_scale * noise[t,e])), product and sum each
+ *       rounded to fp32 as the page's fp32 code does (0.1 on the page);
+ *       `noise` holds the caller's standard-normal draws.
+ *     noisy_logits (NULL ok, [T,E]) receives the routed values.
+ *     Writes topk_idx [T,k] and topk_w [T,k]. */
+enum { MOE_ROUTER_TOPK = 0, MOE_ROUTER_TOP1_FULL = 1 };
+int moe_route_logits_ex(const moe_shape* s, int mode, const float* logits, const float* noise,
+                        float noise_scale, int32_t* topk_idx, float* topk_w,
+                        float* noisy_logits /* NULL ok */, void* stream);
+
+/* 5b. Balance-loss variants over per-expert loads `load` [E] int32:
+ *     mode MOE_LOSS_SHARE: lambda * sum_e (load[e] / (T k)) * (1/E), as
+ *       moe_aux_loss ([EP] section 2.3; pass the kept counts);
+ *     mode MOE_LOSS_VARIANCE: lambda * mean_e (load[e] - mean load)^2, the
+ *       load-variance loss of [PyTorchMoE] section 3.3 item 1 (the stable
+ *       layer of section 4.3 applies it, lambda 0.01, to the top-1 choices:
+ *       pass routed), in fp64, stored as fp32. */
+enum { MOE_LOSS_SHARE = 0, MOE_LOSS_VARIANCE = 1 };
+int moe_aux_loss_ex(const moe_shape* s, int mode, const int32_t* load, float* aux, void* stream);
+
 /* 6. Routing heat map and load telemetry, from topk_idx [T,k] (as written by
  *    moe_route).  [EP] section 3.2 step 1: the experts' co-selection counts
  *    per batch, the input of affinity-aware expert placement; the page calls

@@ -28,6 +28,8 @@ _lib = C.CDLL(LIB_PATH)
 
 MOE_F32, MOE_BF16 = 0, 1
 MOE_WS_PERM, MOE_WS_SLOT, MOE_WS_OFFSETS, MOE_WS_XPERM, MOE_WS_H, MOE_WS_OUT = range(6)
+MOE_ROUTER_TOPK, MOE_ROUTER_TOP1_FULL = 0, 1
+MOE_LOSS_SHARE, MOE_LOSS_VARIANCE = 0, 1
 
 
 class MoeShape(C.Structure):
@@ -63,6 +65,8 @@ _sigs = {
     "moe_combine": (C.c_int, [_SP, _P, _P, _P, _P, _P]),
     "moe_aux_loss": (C.c_int, [_SP, _P, _P, _P]),
     "moe_coactivation": (C.c_int, [_SP, _P, _P, _P, _P, _P]),
+    "moe_route_logits_ex": (C.c_int, [_SP, C.c_int, _P, _P, C.c_float, _P, _P, _P, _P]),
+    "moe_aux_loss_ex": (C.c_int, [_SP, C.c_int, _P, _P, _P]),
     "moe_layer_forward": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                     _P, _Z, _P]),
 }
@@ -167,6 +171,16 @@ def moe_combine(s, out_perm, slot, topk_w, y, stream=None) -> None:
 
 def moe_aux_loss(s, counts, aux, stream=None) -> None:
     _check(_lib.moe_aux_loss(C.byref(s), _ptr(counts), _ptr(aux), _stream(stream)))
+
+
+def moe_route_logits_ex(s, mode, logits, topk_idx, topk_w, noise=None, noise_scale=0.0, noisy_logits=None,
+                        stream=None) -> None:
+    _check(_lib.moe_route_logits_ex(C.byref(s), int(mode), _ptr(logits), _ptr(noise), float(noise_scale),
+                                    _ptr(topk_idx), _ptr(topk_w), _ptr(noisy_logits), _stream(stream)))
+
+
+def moe_aux_loss_ex(s, mode, load, aux, stream=None) -> None:
+    _check(_lib.moe_aux_loss_ex(C.byref(s), int(mode), _ptr(load), _ptr(aux), _stream(stream)))
 
 
 def moe_coactivation(s, topk_idx, H, routed, stats=None, stream=None) -> None:

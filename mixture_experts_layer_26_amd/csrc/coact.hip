@@ -84,9 +84,11 @@ __global__ __launch_bounds__(kCoactThreads) void coact_kernel(const int32_t* __r
         if (lr[e]) atomicAdd(&routed[e], (int)lr[e]);
 }
 
-// one workgroup: mean, population variance and CV of routed[0..E), in fp64
-__global__ __launch_bounds__(256) void load_stats_kernel(const int32_t* __restrict__ routed, int E,
-                                                         float* __restrict__ stats) {
+// mean and population variance of load[0..E) in fp64 by one workgroup of
+// 256 threads (two passes: the mean, then the squared deviations); the
+// results are valid in thread 0
+__device__ __forceinline__ void block_mean_var(const int32_t* __restrict__ routed, int E, double* mean_out,
+                                               double* var_out) {
     __shared__ double part[256 / kWave];
     __shared__ double s_mean;
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
@@ -114,14 +116,37 @@ __global__ __launch_bounds__(256) void load_stats_kernel(const int32_t* __restri
     if (threadIdx.x == 0) {
         double tot = 0.0;
         for (int w = 0; w < 256 / kWave; ++w) tot += part[w];
-        const double var = tot / (double)E;
+        *mean_out = m;
+        *var_out = tot / (double)E;
+    }
+}
+
+// mean, population variance and CV of the loads
+__global__ __launch_bounds__(256) void load_stats_kernel(const int32_t* __restrict__ routed, int E,
+                                                         float* __restrict__ stats) {
+    double m = 0.0, var = 0.0;
+    block_mean_var(routed, E, &m, &var);
+    if (threadIdx.x == 0) {
         stats[0] = (float)m;
         stats[1] = (float)var;
         stats[2] = m > 0.0 ? (float)(sqrt(var) / m) : 0.0f;
     }
 }
 
+// load-variance balance loss ([PyTorchMoE] section 3.3 item 1)
+__global__ __launch_bounds__(256) void aux_variance_kernel(const int32_t* __restrict__ load, int E, float lambda,
+                                                           float* __restrict__ aux) {
+    double m = 0.0, var = 0.0;
+    block_mean_var(load, E, &m, &var);
+    if (threadIdx.x == 0) aux[0] = (float)((double)lambda * var);
+}
+
 }  // namespace
+
+hipError_t launch_aux_variance(int E, float lambda, const int32_t* load, float* aux, hipStream_t st) {
+    hipLaunchKernelGGL(aux_variance_kernel, dim3(1), dim3(256), 0, st, load, E, lambda, aux);
+    return hipGetLastError();
+}
 
 hipError_t launch_coactivation(int64_t T, int k, int E, const int32_t* idx, int32_t* H, int32_t* routed,
                                float* stats, int cus, hipStream_t st) {

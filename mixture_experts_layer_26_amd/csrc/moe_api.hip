@@ -390,6 +390,43 @@ int moe_aux_loss(const moe_shape* s, const int32_t* counts, float* aux, void* st
     return MOE_OK;
 }
 
+int moe_route_logits_ex(const moe_shape* s, int mode, const float* logits, const float* noise, float noise_scale,
+                        int32_t* topk_idx, float* topk_w, float* noisy_logits, void* stream) {
+    Geo g;
+    if (int rc = validate(s, &g)) return rc;
+    if (mode != MOE_ROUTER_TOPK && mode != MOE_ROUTER_TOP1_FULL)
+        return fail(MOE_ERR_SHAPE, "unknown router mode %d", mode);
+    if (mode == MOE_ROUTER_TOP1_FULL && g.k != 1)
+        return fail(MOE_ERR_SHAPE, "MOE_ROUTER_TOP1_FULL needs k = 1 (got k=%lld)", (long long)g.k);
+    if (!std::isfinite(noise_scale)) return fail(MOE_ERR_SHAPE, "noise_scale must be finite");
+    MOE_REQUIRE(logits);
+    MOE_OPTIONAL(noise);
+    MOE_REQUIRE(topk_idx);
+    MOE_REQUIRE(topk_w);
+    MOE_OPTIONAL(noisy_logits);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    RouteArgs a = route_config(g.T, (int)g.d, (int)g.E, (int)g.k, s->temperature, s->dtype, device_cu_count());
+    a.logits = const_cast<float*>(logits);
+    a.idx = topk_idx;
+    a.w = topk_w;
+    MOE_HIP(launch_route_variant(a, mode, noise, noise_scale, noisy_logits, st), "route variant kernel launch");
+    return MOE_OK;
+}
+
+int moe_aux_loss_ex(const moe_shape* s, int mode, const int32_t* load, float* aux, void* stream) {
+    Geo g;
+    if (int rc = validate(s, &g)) return rc;
+    if (mode != MOE_LOSS_SHARE && mode != MOE_LOSS_VARIANCE) return fail(MOE_ERR_SHAPE, "unknown loss mode %d", mode);
+    MOE_REQUIRE(load);
+    MOE_REQUIRE(aux);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (mode == MOE_LOSS_SHARE)
+        MOE_HIP(launch_aux((int)g.E, g.T, (int)g.k, s->aux_lambda, load, aux, st), "aux kernel launch");
+    else
+        MOE_HIP(launch_aux_variance((int)g.E, s->aux_lambda, load, aux, st), "aux variance kernel launch");
+    return MOE_OK;
+}
+
 int moe_coactivation(const moe_shape* s, const int32_t* topk_idx, int32_t* H, int32_t* routed, float* stats,
                      void* stream) {
     Geo g;

@@ -24,6 +24,8 @@ RouteArgs route_config(int64_t T, int d, int E, int k, float tau, int dtype, int
 size_t route_smem_bytes(const RouteArgs& a);
 hipError_t launch_route_gate(const RouteArgs& a, int dtype, hipStream_t st);
 hipError_t launch_route_logits(const RouteArgs& a, hipStream_t st);
+hipError_t launch_route_variant(const RouteArgs& a, int mode, const float* noise, float scale, float* noisy,
+                                hipStream_t st);
 
 // ---- route_mfma.hip (bf16 x, E <= 256): fp32-accurate gate on MFMA ------
 bool route_mfma_supported(int dtype, int E, int k);
@@ -78,6 +80,7 @@ hipError_t launch_aux(int E, int64_t T, int k, float lambda, const int32_t* coun
 // ---- coact.hip: routing heat map and load telemetry -----------------------
 hipError_t launch_coactivation(int64_t T, int k, int E, const int32_t* idx, int32_t* H, int32_t* routed,
                                float* stats, int cus, hipStream_t st);
+hipError_t launch_aux_variance(int E, float lambda, const int32_t* load, float* aux, hipStream_t st);
 
 // device properties (moe_api.hip)
 int device_cu_count();

@@ -23,20 +23,14 @@ __device__ __forceinline__ bool beats(float av, int ai, float bv, int bi) {
     return av > bv || (av == bv && ai < bi);
 }
 
-// Top-k + softmax of one token's logits row[0..E) by a group of G lanes
-// (G a power of two <= 64, groups aligned inside the wave).  NV >= ceil(E/G).
-// Every lane of the wave must call this (shuffles); only `active` groups
-// write.  Lane gl of the group ends up holding the gl-th winner.
+// Top-k + softmax of one token's logits by a group of G lanes (G a power of
+// two <= 64, groups aligned inside the wave); lane gl holds logits
+// v[i] = L[gl + G i], NV >= ceil(E/G).  Every lane of the wave must call this
+// (shuffles); only `active` groups write.  Lane gl of the group ends up
+// holding the gl-th winner.
 template <int NV>
-__device__ __forceinline__ void topk_softmax_group(const float* row, int E, int k, float tau, int G,
-                                                   int gl, bool active, int32_t* idx_out,
-                                                   float* w_out) {
-    float v[NV];
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const int e = gl + G * i;
-        v[i] = (active && e < E) ? row[e] : 0.0f;
-    }
+__device__ __forceinline__ void topk_softmax_regs(const float (&v)[NV], int E, int k, float tau, int G, int gl,
+                                                  bool active, int32_t* idx_out, float* w_out) {
     uint32_t taken = 0;
     float my_v = 0.0f;
     int my_i = 0;
@@ -73,6 +67,54 @@ __device__ __forceinline__ void topk_softmax_group(const float* row, int E, int 
     if (active && gl < k) {
         idx_out[gl] = my_i;
         w_out[gl] = p / z;
+    }
+}
+
+template <int NV>
+__device__ __forceinline__ void topk_softmax_group(const float* row, int E, int k, float tau, int G,
+                                                   int gl, bool active, int32_t* idx_out,
+                                                   float* w_out) {
+    float v[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int e = gl + G * i;
+        v[i] = (active && e < E) ? row[e] : 0.0f;
+    }
+    topk_softmax_regs<NV>(v, E, k, tau, G, gl, active, idx_out, w_out);
+}
+
+// Top-1 over a softmax of all E logits ([PyTorchMoE] sections 2.3, 4.3): the
+// largest logit (ties to the lower index) and, as its weight, its softmax
+// probability 1 / sum_e exp((L_e - L_max) / tau).  Same lane layout as above.
+template <int NV>
+__device__ __forceinline__ void top1_full_softmax_regs(const float (&v)[NV], int E, float tau, int G, int gl,
+                                                       bool active, int32_t* idx_out, float* w_out) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int e = gl + G * i;
+        if (e < E && beats(v[i], e, bv, bi)) {
+            bv = v[i];
+            bi = e;
+        }
+    }
+    for (int off = G >> 1; off > 0; off >>= 1) {
+        const float ov = __shfl_xor(bv, off, kWave);
+        const int oi = __shfl_xor(bi, off, kWave);
+        if (beats(ov, oi, bv, bi)) {
+            bv = ov;
+            bi = oi;
+        }
+    }
+    float z = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+        if (gl + G * i < E) z += expf((v[i] - bv) / tau);
+    for (int off = G >> 1; off > 0; off >>= 1) z += __shfl_xor(z, off, kWave);
+    if (active && gl == 0) {
+        idx_out[0] = bi;
+        w_out[0] = 1.0f / z;
     }
 }
 
@@ -248,6 +290,48 @@ __global__ __launch_bounds__(256) void route_logits_topk_kernel(RouteArgs a) {
                            a.w + (active ? t : 0) * a.k);
 }
 
+// fp32(l + fp32(scale * n)): two roundings, as two fp32 operations; the
+// pragma keeps the compiler from contracting them into one fused
+// multiply-add (one rounding), which routes differently at near-ties
+__device__ __forceinline__ float noisy_logit(float l, float scale, float n) {
+#pragma clang fp contract(off)
+    const float p = scale * n;
+    return l + p;
+}
+
+// Router variants on logits in global memory.  With `noise`, the routed
+// values are the stable layer's exploration noise of [PyTorchMoE] section 4.3
+// in the page's fp32 arithmetic: fp32(L + fp32(scale * n)), product and sum
+// rounded separately (no fused multiply-add); `noisy` (optional) receives
+// them.  mode MOE_ROUTER_TOPK: top-k + softmax over the selected values;
+// MOE_ROUTER_TOP1_FULL (k = 1): top-1 weighted by the full softmax.
+template <int NV>
+__global__ __launch_bounds__(256) void route_variant_kernel(RouteArgs a, int mode, const float* __restrict__ noise,
+                                                           float scale, float* __restrict__ noisy) {
+    const int G = a.G;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int gpw = kWave / G;
+    const int gl = lane & (G - 1), gi = lane / G;
+    const int64_t gwave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+    const int64_t t = gwave * gpw + gi;
+    const bool active = t < a.T;
+    const int64_t base = (active ? t : 0) * a.E;
+    float v[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int e = gl + G * i;
+        const bool in = active && e < a.E;
+        float x = in ? a.logits[base + e] : 0.0f;
+        if (noise != nullptr && in) x = noisy_logit(x, scale, noise[base + e]);
+        if (noisy != nullptr && in) noisy[base + e] = x;
+        v[i] = x;
+    }
+    int32_t* io = a.idx + (active ? t : 0) * a.k;
+    float* wo = a.w + (active ? t : 0) * a.k;
+    if (mode == MOE_ROUTER_TOP1_FULL) top1_full_softmax_regs<NV>(v, a.E, a.tau, G, gl, active, io, wo);
+    else topk_softmax_regs<NV>(v, a.E, a.k, a.tau, G, gl, active, io, wo);
+}
+
 // ---------------------------------------------------------------- host ----
 
 static int route_nv(int E, int G) {
@@ -320,6 +404,21 @@ static hipError_t launch_gate_t(const RouteArgs& a, hipStream_t st) {
 
 hipError_t launch_route_gate(const RouteArgs& a, int dtype, hipStream_t st) {
     return dtype == MOE_BF16 ? launch_gate_t<uint16_t>(a, st) : launch_gate_t<float>(a, st);
+}
+
+hipError_t launch_route_variant(const RouteArgs& a, int mode, const float* noise, float scale, float* noisy,
+                                hipStream_t st) {
+    const int gpw = kWave / a.G;
+    const int64_t waves = (a.T + gpw - 1) / gpw;
+    const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+    switch (route_nv(a.E, a.G)) {
+        case 1: hipLaunchKernelGGL((route_variant_kernel<1>), grid, block, 0, st, a, mode, noise, scale, noisy); break;
+        case 2: hipLaunchKernelGGL((route_variant_kernel<2>), grid, block, 0, st, a, mode, noise, scale, noisy); break;
+        case 4: hipLaunchKernelGGL((route_variant_kernel<4>), grid, block, 0, st, a, mode, noise, scale, noisy); break;
+        case 8: hipLaunchKernelGGL((route_variant_kernel<8>), grid, block, 0, st, a, mode, noise, scale, noisy); break;
+        default: hipLaunchKernelGGL((route_variant_kernel<16>), grid, block, 0, st, a, mode, noise, scale, noisy); break;
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_route_logits(const RouteArgs& a, hipStream_t st) {

@@ -129,3 +129,30 @@ def test_stage_hook_validation(moe):
     arr = (C.c_void_p * 3)()
     with pytest.raises(moe.MoEError):
         moe._check(moe._lib.moe_set_stage_events(arr, 3))
+
+
+def test_router_variant_and_loss_validation(moe):
+    p = 0x10000  # never dereferenced: validation fails first
+    s2 = moe.shape(64, 64, 8, 2, 128)
+    with pytest.raises(moe.MoEError) as ei:          # top-1 full softmax needs k = 1
+        moe.moe_route_logits_ex(s2, moe.MOE_ROUTER_TOP1_FULL, p, p, p, stream=0)
+    assert ei.value.status == 2 and "k = 1" in str(ei.value)
+    s1 = moe.shape(64, 64, 8, 1, 128)
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_route_logits_ex(s1, 7, p, p, p, stream=0)
+    assert ei.value.status == 2
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_route_logits_ex(s1, moe.MOE_ROUTER_TOP1_FULL, p, p, p, noise=p, noise_scale=float("nan"), stream=0)
+    assert ei.value.status == 2
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_route_logits_ex(s1, moe.MOE_ROUTER_TOP1_FULL, p, p, p, noise=p + 4, noise_scale=0.1, stream=0)
+    assert ei.value.status == 4
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_aux_loss_ex(s1, 5, p, p, stream=0)
+    assert ei.value.status == 2
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_aux_loss_ex(s1, moe.MOE_LOSS_VARIANCE, None, p, stream=0)
+    assert ei.value.status == 1
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_coactivation(s1, p, None, p, stream=0)
+    assert ei.value.status == 1
