@@ -53,6 +53,7 @@ def lib():
         L.oracle_coactivation.argtypes = [_I64, _I64, _I64, _P, _P, _P]
         L.oracle_noisy_logits.argtypes = [_I64, _P, _P, C.c_float, _P]
         L.oracle_route_top1_full.argtypes = [_I64, _I64, C.c_double, _P, _P, _P]
+        L.oracle_window_aux.argtypes = [_I64] * 5 + [_P, C.c_double, _P, _P]
         L.oracle_aux_variance.restype = C.c_double
         L.oracle_aux_variance.argtypes = [_I64, _P, C.c_double]
         L.oracle_load_stats.argtypes = [_I64, _P, _P, _P, _P]
@@ -193,6 +194,17 @@ def route_top1_full(logits32, tau: float = 1.0):
     w = np.empty((T, 1), np.float64)
     lib().oracle_route_top1_full(T, E, float(tau), _p(L), _p(idx), _p(w))
     return idx, w
+
+
+def window_aux(counts_seq, T: int, k: int, W: int, lam: float):
+    """Sliding-window balance loss after each of n batches: (aux [n], pbar
+    [n, E]) in float64, from the per-batch counts [n, E]."""
+    c = _c(counts_seq, np.int32)
+    n, E = c.shape
+    aux = np.empty(n, np.float64)
+    pbar = np.empty((n, E), np.float64)
+    lib().oracle_window_aux(n, E, T, k, W, _p(c), float(lam), _p(aux), _p(pbar))
+    return aux, pbar
 
 
 def aux_variance(load, lam: float) -> float:

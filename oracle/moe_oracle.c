@@ -372,6 +372,27 @@ void oracle_load_stats(int64_t E, const int64_t* load, double* mean, double* var
     *cv = m > 0.0 ? sqrt(*var) / m : 0.0;
 }
 
+/* Balance loss over a sliding window of batches, [EP] section 2.3: the share
+ * p_e of each expert is averaged over the last W batches (W = 100 on the
+ * page) before lambda * sum_e p_e q_e, q_e = 1/E, is taken.  counts holds the
+ * per-expert counts of n successive batches, [n][E]; after batch b the
+ * window is batches max(0, b-W+1) .. b.  Writes aux[b] and pbar[b][E]. */
+void oracle_window_aux(int64_t n, int64_t E, int64_t T, int64_t k, int64_t W, const int32_t* counts,
+                       double lam, double* aux, double* pbar) {
+    for (int64_t b = 0; b < n; ++b) {
+        int64_t first = b - W + 1 < 0 ? 0 : b - W + 1;
+        double m = (double)(b - first + 1);
+        double s = 0.0;
+        for (int64_t e = 0; e < E; ++e) {
+            double acc = 0.0;
+            for (int64_t c = first; c <= b; ++c) acc += (double)counts[c * E + e] / ((double)T * (double)k);
+            pbar[b * E + e] = acc / m;
+            s += pbar[b * E + e] * (1.0 / (double)E);
+        }
+        aux[b] = lam * s;
+    }
+}
+
 /* Whole layer, oracle-only mode: the routing uses the oracle's own logits
  * rounded to float32 (the precision the routing decision is taken in). */
 void oracle_layer_forward(int64_t T, int64_t d, int64_t E, int64_t k, int64_t dff,

@@ -438,3 +438,31 @@ def test_aux_variance_closed_forms(orc):
     assert orc.aux_variance(np.full(E, 7, np.int64), lam) == 0.0
     load = _rng(6).integers(0, 500, 33).astype(np.int64)
     assert math.isclose(orc.aux_variance(load, 0.5), 0.5 * statistics.pvariance(load.tolist()), rel_tol=1e-12)
+
+
+# ---- sliding-window balance loss ([EP] 2.3) and the dense soft workload ----
+
+def test_window_aux_worked_example(orc):
+    """T = 10, k = 1, E = 2, W = 3; counts per batch (10,0), (0,10), (5,5),
+    (10,0), (10,0), (10,0): the window means worked out by hand."""
+    c = np.array([[10, 0], [0, 10], [5, 5], [10, 0], [10, 0], [10, 0]], np.int32)
+    aux, pbar = orc.window_aux(c, T=10, k=1, W=3, lam=1.0)
+    want = [[1.0, 0.0], [0.5, 0.5], [0.5, 0.5], [0.5, 0.5], [25 / 30, 5 / 30], [1.0, 0.0]]
+    assert np.allclose(pbar, want, rtol=0, atol=1e-15)
+    # the shares of every window sum to 1 here, so aux = lambda / E throughout
+    assert np.allclose(aux, 0.5, rtol=0, atol=1e-15)
+
+
+def test_window_aux_reduces_to_the_per_batch_loss(orc):
+    r = _rng(12)
+    E, T, k, lam = 16, 4096, 2, 0.01
+    c = r.integers(0, 600, (30, E)).astype(np.int32)
+    aux1, pbar1 = orc.window_aux(c, T, k, 1, lam)            # W = 1: each batch alone
+    for b in range(30):
+        assert math.isclose(aux1[b], orc.aux(c[b], T, k, lam), rel_tol=1e-13)
+        assert np.allclose(pbar1[b], c[b] / (T * k), rtol=1e-15, atol=0)
+    same = np.tile(c[:1], (250, 1))                          # constant batches: any W
+    auxw, _ = orc.window_aux(same, T, k, 100, lam)
+    assert np.allclose(auxw, orc.aux(c[0], T, k, lam), rtol=1e-13, atol=0)
+    auxw, pbarw = orc.window_aux(c, T, k, 7, lam)            # a window mean of batch shares
+    assert np.allclose(pbarw[20], c[14:21].mean(axis=0) / (T * k), rtol=1e-13, atol=0)
