@@ -212,6 +212,23 @@ int moe_route_logits_ex(const moe_shape* s, int mode, const float* logits, const
 enum { MOE_LOSS_SHARE = 0, MOE_LOSS_VARIANCE = 1 };
 int moe_aux_loss_ex(const moe_shape* s, int mode, const int32_t* load, float* aux, void* stream);
 
+/* 5c. Balance loss over a sliding window of calls ([EP] section 2.3: the
+ *     expert shares are averaged over the last W batches, W = 100 on the
+ *     page, before the loss is taken).  `state` is caller-owned device
+ *     memory of moe_window_state_bytes(E, W) bytes, all zero before the
+ *     first call (the caller clears it, e.g. torch.zeros); it holds the call
+ *     count, the per-expert window sums and the last W count vectors, and
+ *     must not be shared by calls that are not ordered on one stream.  Each
+ *     call appends `counts` [E] (the kept counts of this batch) and writes
+ *       pbar[e] = (sum of counts[e] over the last min(n, W) calls, this one
+ *                  included) / (min(n, W) * T * k)          (NULL ok, fp32)
+ *       aux     = lambda * sum_e pbar[e] * (1/E)
+ *     in fp64, stored as fp32.  1 <= W <= 2^20.  The state's size depends
+ *     only on E and W; a shape with other E or W must use its own state. */
+size_t moe_window_state_bytes(int64_t E, int64_t W);
+int moe_aux_loss_window(const moe_shape* s, const int32_t* counts, void* state, int64_t W, float* aux,
+                        float* pbar /* NULL ok, [E] */, void* stream);
+
 /* 6. Routing heat map and load telemetry, from topk_idx [T,k] (as written by
  *    moe_route).  [EP] section 3.2 step 1: the experts' co-selection counts
  *    per batch, the input of affinity-aware expert placement; the page calls

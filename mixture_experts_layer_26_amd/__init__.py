@@ -67,6 +67,8 @@ _sigs = {
     "moe_coactivation": (C.c_int, [_SP, _P, _P, _P, _P, _P]),
     "moe_route_logits_ex": (C.c_int, [_SP, C.c_int, _P, _P, C.c_float, _P, _P, _P, _P]),
     "moe_aux_loss_ex": (C.c_int, [_SP, C.c_int, _P, _P, _P]),
+    "moe_window_state_bytes": (C.c_size_t, [C.c_int64, C.c_int64]),
+    "moe_aux_loss_window": (C.c_int, [_SP, _P, _P, C.c_int64, _P, _P, _P]),
     "moe_layer_forward": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                     _P, _Z, _P]),
 }
@@ -181,6 +183,24 @@ def moe_route_logits_ex(s, mode, logits, topk_idx, topk_w, noise=None, noise_sca
 
 def moe_aux_loss_ex(s, mode, load, aux, stream=None) -> None:
     _check(_lib.moe_aux_loss_ex(C.byref(s), int(mode), _ptr(load), _ptr(aux), _stream(stream)))
+
+
+def moe_window_state_bytes(E: int, W: int) -> int:
+    return int(_lib.moe_window_state_bytes(int(E), int(W)))
+
+
+def window_state(E: int, W: int, device="cuda"):
+    """A zeroed window state for moe_aux_loss_window."""
+    import torch
+    n = moe_window_state_bytes(E, W)
+    if n == 0:
+        raise MoEError(2, f"invalid window: E={E}, W={W}")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def moe_aux_loss_window(s, counts, state, W, aux, pbar=None, stream=None) -> None:
+    _check(_lib.moe_aux_loss_window(C.byref(s), _ptr(counts), _ptr(state), int(W), _ptr(aux), _ptr(pbar),
+                                    _stream(stream)))
 
 
 def moe_coactivation(s, topk_idx, H, routed, stats=None, stream=None) -> None:

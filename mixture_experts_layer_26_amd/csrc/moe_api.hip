@@ -427,6 +427,26 @@ int moe_aux_loss_ex(const moe_shape* s, int mode, const int32_t* load, float* au
     return MOE_OK;
 }
 
+size_t moe_window_state_bytes(int64_t E, int64_t W) {
+    if (E < 1 || E > 1024 || W < 1 || W > (int64_t(1) << 20)) return 0;
+    return window_state_bytes(E, W);
+}
+
+int moe_aux_loss_window(const moe_shape* s, const int32_t* counts, void* state, int64_t W, float* aux, float* pbar,
+                        void* stream) {
+    Geo g;
+    if (int rc = validate(s, &g)) return rc;
+    if (W < 1 || W > (int64_t(1) << 20)) return fail(MOE_ERR_SHAPE, "W must be in [1, 2^20] (got %lld)", (long long)W);
+    MOE_REQUIRE(counts);
+    MOE_REQUIRE(state);
+    MOE_REQUIRE(aux);
+    MOE_OPTIONAL(pbar);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    MOE_HIP(launch_window_aux((int)g.E, W, g.T, (int)g.k, s->aux_lambda, counts, state, aux, pbar, st),
+            "window loss kernel launch");
+    return MOE_OK;
+}
+
 int moe_coactivation(const moe_shape* s, const int32_t* topk_idx, int32_t* H, int32_t* routed, float* stats,
                      void* stream) {
     Geo g;

@@ -82,6 +82,11 @@ hipError_t launch_coactivation(int64_t T, int k, int E, const int32_t* idx, int3
                                float* stats, int cus, hipStream_t st);
 hipError_t launch_aux_variance(int E, float lambda, const int32_t* load, float* aux, hipStream_t st);
 
+// ---- window_loss.hip: balance loss over a sliding window of calls ---------
+size_t window_state_bytes(int64_t E, int64_t W);
+hipError_t launch_window_aux(int E, int64_t W, int64_t T, int k, float lambda, const int32_t* counts, void* state,
+                             float* aux, float* pbar, hipStream_t st);
+
 // device properties (moe_api.hip)
 int device_cu_count();
 

@@ -123,6 +123,13 @@ _add(MoEConfig("ragged_large_even", T=32768, d=1000, E=8, k=2, d_ff=1976,
                capacity_factor=1.1, bias_std=0.1, gate_bias_std=0.5,
                note="even K-step counts (32, 62) with a partial last step"))
 
+# dense soft MoE ([EP] section 2.2): every token weighted over all experts
+# by softmax(logits / 0.2); k = E with no capacity limit, 4096 rows per
+# expert, so the grouped GEMMs run in their matrix-core-bound regime
+_add(MoEConfig("dense_soft_e16", T=4096, d=1024, E=16, k=16, d_ff=4096,
+               capacity_factor=0.0, temperature=0.2,
+               note="k = E: the soft MoE of every expert, 4096 rows each"))
+
 # limits of the library: E = 1024 experts, k = 32 choices per token
 _add(MoEConfig("max_experts", T=2048, d=64, E=1024, k=4, d_ff=64,
                capacity_factor=1.0, bias_std=0.1))
