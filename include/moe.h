@@ -117,8 +117,14 @@ size_t moe_workspace_size(const moe_shape* s);
  * moe_layer_forward leaves there, for inspection after the call completes:
  * which = MOE_WS_PERM (int32 [max_rows]), MOE_WS_SLOT (int32 [T,k]),
  * MOE_WS_OFFSETS (int32 [E+1]), MOE_WS_XPERM (dtype [max_rows,d]),
- * MOE_WS_H (dtype [max_rows,d_ff]), MOE_WS_OUT (fp32 [max_rows,d], the
- * expert outputs before the weighted sum).  -1 if invalid. */
+ * MOE_WS_H (h; fp32 layers: [max_rows,d_ff] row-major; bf16 layers: 16-row x
+ * 32-column tiles over expert segments that start at multiples of 16 rows --
+ * expert e's local row i is padded row p = P[e] + i with P[e] the sum of the
+ * earlier experts' counts rounded up to 16, and (p, c) is element
+ * ((p/16)*ceil(d_ff/32) + c/32)*512 + (p%16)*32 + c%32; padding rows are
+ * undefined, columns d_ff..32*ceil(d_ff/32)-1 are zero), MOE_WS_OUT (fp32
+ * [max_rows,d], the expert outputs before the weighted sum).  -1 if
+ * invalid. */
 enum { MOE_WS_PERM = 0, MOE_WS_SLOT = 1, MOE_WS_OFFSETS = 2, MOE_WS_XPERM = 3, MOE_WS_H = 4,
        MOE_WS_OUT = 5 };
 int64_t moe_workspace_offset(const moe_shape* s, int which);

@@ -120,7 +120,9 @@ static WsLayout ws_layout(const Geo& g) {
     L.perm = take(sizeof(int32_t) * (size_t)g.max_rows);
     L.slot = take(sizeof(int32_t) * (size_t)(g.T * g.k));
     L.xperm = take((size_t)g.esz * (size_t)g.max_rows * g.d);
-    L.h = take((size_t)g.esz * (size_t)g.max_rows * g.dff);
+    // bf16: h in 16 x 32 tiles over 16-row-padded expert segments (ffn_bf16.hip)
+    L.h = take(g.esz == 2 ? (size_t)g.esz * (size_t)h_tiled_rows(g.max_rows, g.E) * (size_t)((g.dff + 31) / 32 * 32)
+                          : (size_t)g.esz * (size_t)g.max_rows * g.dff);
     L.out = take(sizeof(float) * (size_t)g.max_rows * g.d);
     L.total = p;
     return L;

@@ -66,7 +66,12 @@ struct GemmArgs {
     const int32_t* offsets;  // [E+1] row segments of the experts
     int E, K, N;
     void* out;               // EPI_GELU_H: [rows, N] dtype; EPI_STORE_F32: [rows, N] fp32
+    // bf16 kernels: the EPI_GELU_H output and the EPI_STORE_F32 input A are h
+    // in the tile layout of ffn_bf16.hip (h_tiled_rows rows); fp32 kernels:
+    // row-major
 };
+// rows of the h tile layout for max_rows packed rows over E experts
+inline int64_t h_tiled_rows(int64_t max_rows, int64_t E) { return ((max_rows + 15 * E + 15) / 16) * 16; }
 hipError_t launch_ffn_gemm_bf16(const GemmArgs& g, int epi, int64_t max_rows, hipStream_t st);
 hipError_t launch_ffn_gemm_f32(const GemmArgs& g, int epi, hipStream_t st);
 
