@@ -54,6 +54,8 @@ def lib():
         L.oracle_noisy_logits.argtypes = [_I64, _P, _P, C.c_float, _P]
         L.oracle_route_top1_full.argtypes = [_I64, _I64, C.c_double, _P, _P, _P]
         L.oracle_window_aux.argtypes = [_I64] * 5 + [_P, C.c_double, _P, _P]
+        L.oracle_ffn_backward_rows.argtypes = [_I64, _P, _P, _P, _I64, _I64, C.c_int] + [_P] * 12
+        L.oracle_route_backward.argtypes = [_I64, _I64, _I64, _I64, C.c_double, C.c_int] + [_P] * 9
         L.oracle_aux_variance.restype = C.c_double
         L.oracle_aux_variance.argtypes = [_I64, _P, C.c_double]
         L.oracle_load_stats.argtypes = [_I64, _P, _P, _P, _P]
@@ -205,6 +207,67 @@ def window_aux(counts_seq, T: int, k: int, W: int, lam: float):
     pbar = np.empty((n, E), np.float64)
     lib().oracle_window_aux(n, E, T, k, W, _p(c), float(lam), _p(aux), _p(pbar))
     return aux, pbar
+
+
+def ffn_backward_rows(tok, exp_id, wt, x, W1, b1, W2, b2, dy, E: int):
+    """Backward of the expert FFN over listed kept rows (token, expert,
+    routing weight): (dw [n], dxp [n,d], dW1, db1, dW2, db2), float64, the
+    weight gradients summed over the listed rows only."""
+    tok, exp_id = _c(tok, np.int32), _c(exp_id, np.int32)
+    wt = _c(wt, np.float64)
+    x, W1, W2 = _c(x), _c(W1), _c(W2)
+    b1, b2, dy = _c(b1, np.float32), _c(b2, np.float32), _c(dy, np.float32)
+    d, dff = x.shape[1], W1.shape[2]
+    n = len(tok)
+    dw = np.zeros(n, np.float64)
+    dxp = np.zeros((n, d), np.float64)
+    dW1 = np.zeros((E, d, dff), np.float64)
+    db1 = np.zeros((E, dff), np.float64)
+    dW2 = np.zeros((E, dff, d), np.float64)
+    db2 = np.zeros((E, d), np.float64)
+    lib().oracle_ffn_backward_rows(n, _p(tok), _p(exp_id), _p(wt), d, dff, _dtype_code(x), _p(x), _p(W1),
+                                   _p(b1), _p(W2), _p(b2), _p(dy), _p(dw), _p(dxp), _p(dW1), _p(db1),
+                                   _p(dW2), _p(db2))
+    return dw, dxp, dW1, db1, dW2, db2
+
+
+def route_backward(x, Wg, idx, w, dw, tau: float):
+    """Gate backward from the routing-weight gradients dw [T,k]: (dl [T,E],
+    dWg [d,E], dbg [E], dxg [T,d]), float64."""
+    x, Wg = _c(x), _c(Wg, np.float32)
+    idx, w, dw = _c(idx, np.int32), _c(w, np.float64), _c(dw, np.float64)
+    T, d = x.shape
+    E = Wg.shape[1]
+    k = idx.shape[1]
+    dl = np.empty((T, E), np.float64)
+    dWg = np.empty((d, E), np.float64)
+    dbg = np.empty(E, np.float64)
+    dxg = np.empty((T, d), np.float64)
+    lib().oracle_route_backward(T, d, E, k, float(tau), _dtype_code(x), _p(x), _p(Wg), _p(idx), _p(w), _p(dw),
+                                _p(dl), _p(dWg), _p(dbg), _p(dxg))
+    return dl, dWg, dbg, dxg
+
+
+def layer_backward(x, Wg, W1, b1, W2, b2, logits32, k: int, cf: float, tau: float, dy):
+    """Gradients of sum(dy * y) for the layer routed on the fp32 logits
+    `logits32`: the selection, capacity and drops are fixed by them; the
+    routing weights, expert FFNs and the gate are differentiated.  Returns a
+    dict of float64 arrays: dx, dWg, dbg, dW1, db1, dW2, db2, plus dw, dl."""
+    T, d = np.asarray(x).shape
+    E = np.asarray(Wg).shape[1]
+    idx, w = route(logits32, k, tau)
+    dsp = dispatch(idx, E, capacity(T, E, k, cf))
+    slot = dsp["slot"]
+    tt, jj = np.nonzero(slot >= 0)
+    dw = np.zeros((T, k), np.float64)
+    dwr, dxp, dW1, db1, dW2, db2 = ffn_backward_rows(tt.astype(np.int32), idx[tt, jj], w[tt, jj], x, W1, b1, W2,
+                                                     b2, dy, E)
+    dw[tt, jj] = dwr
+    dx = np.zeros((T, d), np.float64)
+    np.add.at(dx, tt, dxp)
+    dl, dWg, dbg, dxg = route_backward(x, Wg, idx, w, dw, tau)
+    return dict(dx=dx + dxg, dWg=dWg, dbg=dbg, dW1=dW1, db1=db1, dW2=dW2, db2=db2, dw=dw, dl=dl,
+                idx=idx, slot=slot)
 
 
 def aux_variance(load, lam: float) -> float:

@@ -31,6 +31,7 @@
  * bit patterns.  Every element is converted exactly to double before use.
  * Inputs must be finite.
  */
+#define _GNU_SOURCE
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -326,6 +327,122 @@ void oracle_layer_tokens(int64_t n, const int32_t* toks, int64_t d, int64_t dff,
     free(o);
     free(re);
     free(rt);
+}
+
+/* Derivative of the exact GELU: d/du [u Phi(u)] = Phi(u) + u phi(u). */
+static double orc_gelu_grad(double u) {
+    return 0.5 * (1.0 + erf(u / sqrt(2.0))) + u * exp(-0.5 * u * u) / sqrt(2.0 * M_PI);
+}
+
+/* Backward of the expert FFN for listed kept rows.  Row i is token tok[i]
+ * routed to expert exp_id[i] with routing weight wt[i]; with
+ *   a = W1[e]^T x + b1[e],  h = GELU(a),  o = W2[e]^T h + b2[e]
+ * and the row's upstream gradient g = wt[i] * dy[tok[i]] (the combine adds
+ * w * o into y, [PithTrain] section 4.1):
+ *   dw[i]   = dy[tok] . o                  (gradient w.r.t. the routing weight)
+ *   dW2[e] += h g^T,  db2[e] += g,  dh = W2[e] g,  da = dh * GELU'(a),
+ *   dW1[e] += x da^T, db1[e] += da,  dxp[i] = W1[e] da   (gradient w.r.t. x)
+ * dW1 [E,d,dff], db1 [E,dff], dW2 [E,dff,d], db2 [E,d] are accumulated (the
+ * caller zeroes them); experts without rows keep their zeros, which is the
+ * expert-grained gradient of [EP] section 4.3 (inactive experts get none).
+ * Rows are taken in order; the loops inside a row run in parallel over
+ * disjoint outputs. */
+void oracle_ffn_backward_rows(int64_t n, const int32_t* tok, const int32_t* exp_id, const double* wt,
+                              int64_t d, int64_t dff, int dtype, const void* x, const void* W1,
+                              const float* b1, const void* W2, const float* b2, const float* dy,
+                              double* dw, double* dxp, double* dW1, double* db1, double* dW2, double* db2) {
+    double* a = (double*)malloc((size_t)dff * sizeof(double));
+    double* h = (double*)malloc((size_t)dff * sizeof(double));
+    double* da = (double*)malloc((size_t)dff * sizeof(double));
+    double* xr = (double*)malloc((size_t)d * sizeof(double));
+    double* g = (double*)malloc((size_t)d * sizeof(double));
+    for (int64_t i = 0; i < n; ++i) {
+        const int64_t t = tok[i], e = exp_id[i];
+        const int64_t w1 = e * d * dff, w2 = e * dff * d;
+        for (int64_t c = 0; c < d; ++c) {
+            xr[c] = elem(x, dtype, t * d + c);
+            g[c] = wt[i] * (double)dy[t * d + c];
+        }
+#pragma omp parallel for schedule(static)
+        for (int64_t f = 0; f < dff; ++f) {
+            double acc = (double)b1[e * dff + f];
+            for (int64_t c = 0; c < d; ++c) acc += xr[c] * elem(W1, dtype, w1 + c * dff + f);
+            a[f] = acc;
+            h[f] = oracle_gelu(acc);
+        }
+        double dot = 0.0;
+#pragma omp parallel for schedule(static) reduction(+ : dot)
+        for (int64_t c = 0; c < d; ++c) {
+            double o = (double)b2[e * d + c];
+            for (int64_t f = 0; f < dff; ++f) o += h[f] * elem(W2, dtype, w2 + f * d + c);
+            dot += (double)dy[t * d + c] * o;
+        }
+        dw[i] = dot;
+#pragma omp parallel for schedule(static)
+        for (int64_t f = 0; f < dff; ++f) {
+            double dh = 0.0;
+            for (int64_t c = 0; c < d; ++c) {
+                dh += elem(W2, dtype, w2 + f * d + c) * g[c];
+                dW2[w2 + f * d + c] += h[f] * g[c];
+            }
+            da[f] = dh * orc_gelu_grad(a[f]);
+            db1[e * dff + f] += da[f];
+        }
+#pragma omp parallel for schedule(static)
+        for (int64_t c = 0; c < d; ++c) {
+            db2[e * d + c] += g[c];
+            double acc = 0.0;
+            for (int64_t f = 0; f < dff; ++f) {
+                acc += elem(W1, dtype, w1 + c * dff + f) * da[f];
+                dW1[w1 + c * dff + f] += xr[c] * da[f];
+            }
+            dxp[i * d + c] = acc;
+        }
+    }
+    free(g);
+    free(xr);
+    free(da);
+    free(h);
+    free(a);
+}
+
+/* Backward of the gate ([PithTrain] section 4.1: w = softmax over the k
+ * selected logits, [EP] section 2.2: divided by tau).  The selection itself
+ * is piecewise constant, so only the selected logits get gradient:
+ *   dl[t, idx_j] = w_j (dw_j - sum_i w_i dw_i) / tau,  0 for the others;
+ * then through the linear gate: dWg[i][e] = sum_t x[t][i] dl[t][e],
+ * dbg[e] = sum_t dl[t][e], dxg[t][i] = sum_e Wg[i][e] dl[t][e].
+ * w and dw are [T,k] in double (dw of a dropped slot is 0). */
+void oracle_route_backward(int64_t T, int64_t d, int64_t E, int64_t k, double tau, int dtype, const void* x,
+                           const float* Wg, const int32_t* idx, const double* w, const double* dw, double* dl,
+                           double* dWg, double* dbg, double* dxg) {
+    for (int64_t t = 0; t < T; ++t) {
+        double s = 0.0;
+        for (int64_t j = 0; j < k; ++j) s += w[t * k + j] * dw[t * k + j];
+        for (int64_t e = 0; e < E; ++e) dl[t * E + e] = 0.0;
+        for (int64_t j = 0; j < k; ++j) dl[t * E + idx[t * k + j]] = w[t * k + j] * (dw[t * k + j] - s) / tau;
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < d; ++i) {
+        for (int64_t e = 0; e < E; ++e) {
+            double acc = 0.0;
+            for (int64_t t = 0; t < T; ++t) acc += elem(x, dtype, t * d + i) * dl[t * E + e];
+            dWg[i * E + e] = acc;
+        }
+    }
+    for (int64_t e = 0; e < E; ++e) {
+        double acc = 0.0;
+        for (int64_t t = 0; t < T; ++t) acc += dl[t * E + e];
+        dbg[e] = acc;
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t i = 0; i < d; ++i) {
+            double acc = 0.0;
+            for (int64_t e = 0; e < E; ++e) acc += (double)Wg[i * E + e] * dl[t * E + e];
+            dxg[t * d + i] = acc;
+        }
+    }
 }
 
 /* Balance loss lambda * sum_e p_e q_e, p_e = counts[e] / (T k), q_e = 1/E.

@@ -466,3 +466,99 @@ def test_window_aux_reduces_to_the_per_batch_loss(orc):
     assert np.allclose(auxw, orc.aux(c[0], T, k, lam), rtol=1e-13, atol=0)
     auxw, pbarw = orc.window_aux(c, T, k, 7, lam)            # a window mean of batch shares
     assert np.allclose(pbarw[20], c[14:21].mean(axis=0) / (T * k), rtol=1e-13, atol=0)
+
+
+# ---- backward ([EP] 4.3: gradients for the active experts only) ----
+
+def _fd_setup(seed=21, T=7, d=8, E=5, k=2, dff=12, cf=0.6, tau=0.7):
+    """Small fp32 layer with biases, one drop-inducing capacity and expert 4
+    made inactive by a very negative gate bias; no near-ties in the routing."""
+    r = _rng(seed)
+    while True:
+        x = r.standard_normal((T, d)).astype(np.float32)
+        Wg = (r.standard_normal((d, E)) / math.sqrt(d)).astype(np.float32)
+        bg = np.array([0.3, -0.2, 0.1, 0.0, -50.0], np.float32)[:E]
+        L = x.astype(np.float64) @ Wg.astype(np.float64) + bg
+        srt = np.sort(L, axis=1)[:, ::-1]
+        if np.min(srt[:, k - 1] - srt[:, k]) > 0.05:
+            break
+    W1 = (r.standard_normal((E, d, dff)) / math.sqrt(d)).astype(np.float32)
+    b1 = (0.1 * r.standard_normal((E, dff))).astype(np.float32)
+    W2 = (r.standard_normal((E, dff, d)) / math.sqrt(dff)).astype(np.float32)
+    b2 = (0.1 * r.standard_normal((E, d))).astype(np.float32)
+    dy = r.standard_normal((T, d)).astype(np.float32)
+    return dict(x=x, Wg=Wg, bg=bg, W1=W1, b1=b1, W2=W2, b2=b2, dy=dy, k=k, cf=cf, tau=tau)
+
+
+def _fd_loss(orc, p, idx, slot):
+    """sum(dy * y) with the routing decisions fixed and w from fp64 logits."""
+    L = orc.gate(p["x"], p["Wg"], p["bg"])
+    sel = np.take_along_axis(L, idx, 1) / p["tau"]
+    sel -= sel.max(axis=1, keepdims=True)
+    w = np.exp(sel)
+    w /= w.sum(axis=1, keepdims=True)
+    tt, jj = np.nonzero(slot >= 0)
+    o = orc.ffn_rows(tt.astype(np.int32), idx[tt, jj], p["x"], p["W1"], p["b1"], p["W2"], p["b2"])
+    y = np.zeros(p["x"].shape, np.float64)
+    np.add.at(y, tt, w[tt, jj][:, None] * o)
+    return float((p["dy"].astype(np.float64) * y).sum())
+
+
+def test_layer_backward_matches_finite_differences(orc):
+    p = _fd_setup()
+    L32 = orc.gate(p["x"], p["Wg"], p["bg"]).astype(np.float32)
+    g = orc.layer_backward(p["x"], p["Wg"], p["W1"], p["b1"], p["W2"], p["b2"], L32, p["k"], p["cf"], p["tau"],
+                           p["dy"])
+    assert (g["slot"] < 0).any(), "the capacity should drop a slot"
+    # the gate bias gradient is the column sum of dl (the bias adds into every logit)
+    g["dbg_check"] = g["dl"].sum(axis=0)
+    assert np.allclose(g["dbg"], g["dbg_check"], rtol=1e-12, atol=1e-15)
+    r = _rng(5)
+    names = {"x": "dx", "Wg": "dWg", "bg": "dbg", "W1": "dW1", "b1": "db1", "W2": "dW2", "b2": "db2"}
+    for name, gname in names.items():
+        arr = p[name]
+        for _ in range(6):
+            i = tuple(int(r.integers(0, s)) for s in arr.shape)
+            if name in ("W1", "b1", "W2", "b2") and i[0] == 4:
+                i = (int(r.integers(0, 4)),) + i[1:]
+            v = arr[i]
+            hi, lo = np.float32(v + np.float32(1e-3)), np.float32(v - np.float32(1e-3))
+            arr[i] = hi
+            f_hi = _fd_loss(orc, p, g["idx"], g["slot"])
+            arr[i] = lo
+            f_lo = _fd_loss(orc, p, g["idx"], g["slot"])
+            arr[i] = v
+            fd = (f_hi - f_lo) / (float(hi) - float(lo))
+            assert abs(fd - g[gname][i]) <= 2e-6 * max(1.0, abs(fd)), (name, i, fd, g[gname][i])
+
+
+def test_backward_inactive_expert_and_dropped_slots(orc):
+    p = _fd_setup()
+    L32 = orc.gate(p["x"], p["Wg"], p["bg"]).astype(np.float32)
+    g = orc.layer_backward(p["x"], p["Wg"], p["W1"], p["b1"], p["W2"], p["b2"], L32, p["k"], p["cf"], p["tau"],
+                           p["dy"])
+    assert not (g["idx"] == 4).any()
+    for name in ("dW1", "db1", "dW2", "db2"):
+        assert not g[name][4].any(), name          # expert-grained: no gradient for an idle expert
+    assert np.all(g["dw"][g["slot"] < 0] == 0.0)   # a dropped slot's output does not depend on its weight
+    # softmax over the selected logits: its gradient sums to zero over each token's choices
+    assert np.allclose(g["dl"].sum(axis=1), 0.0, atol=1e-13)
+
+
+def test_gelu_derivative_closed_forms(orc):
+    # GELU'(0) = 1/2; GELU'(u) + GELU'(-u) = 1 (Phi(u) + Phi(-u) = 1, the u phi terms cancel)
+    d, dff = 1, 1
+    x = np.array([[0.0], [1.3], [-1.3]], np.float32)
+    W1 = np.ones((1, d, dff), np.float32)
+    W2 = np.ones((1, dff, d), np.float32)
+    b = np.zeros((1, 1), np.float32)
+    dy = np.ones((3, 1), np.float32)
+    _, dxp, _, _, _, _ = orc.ffn_backward_rows(np.arange(3, dtype=np.int32), np.zeros(3, np.int32),
+                                               np.ones(3), x, W1, b, W2, b, dy, 1)
+    assert math.isclose(dxp[0, 0], 0.5, rel_tol=1e-15)
+    assert math.isclose(dxp[1, 0] + dxp[2, 0], 1.0, rel_tol=1e-14)
+    # against the normal CDF and density from the statistics module
+    from statistics import NormalDist
+    nd = NormalDist()
+    u = float(x[1, 0])
+    assert math.isclose(dxp[1, 0], nd.cdf(u) + u * nd.pdf(u), rel_tol=1e-12)
