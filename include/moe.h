@@ -265,6 +265,36 @@ int moe_layer_forward(const moe_shape* s, const void* x, const float* Wg, const 
                       int32_t* routed, int32_t* topk_idx, float* topk_w, float* logits,
                       void* ws, size_t ws_bytes, void* stream);
 
+/* ---- backward ------------------------------------------------------------
+ * Gradients of sum(dy * y) for one forward call, with its routing decisions
+ * (selection, capacity, drops) fixed: they are piecewise constant.  The
+ * layer is differentiated as autograd would differentiate [PithTrain]
+ * section 4.1's layer: the combine y[t] += w[t,j] o[r], the expert FFN
+ * o = GELU(x W1 + b1) W2 + b2 (exact erf GELU, derivative Phi(a) + a phi(a))
+ * and the gate w = softmax(l_sel / temperature) with l = x Wg + bg; the
+ * balance loss depends on integer counts only and has no gradient.  Experts
+ * that received no row get zero weight and bias gradients ([EP] section
+ * 4.3, expert-grained gradients).
+ * Inputs from the forward call: topk_idx, topk_w, slot, offsets, x_perm
+ * (dtype [max_rows,d]) and out_perm (fp32 [max_rows,d], the expert outputs
+ * before the weighted sum) -- the outputs of moe_route / moe_dispatch /
+ * moe_grouped_ffn, or the regions MOE_WS_SLOT, MOE_WS_OFFSETS,
+ * MOE_WS_XPERM, MOE_WS_OUT of a moe_layer_forward workspace (pass the
+ * forward's topk_idx and topk_w outputs).  dy [T,d] fp32.
+ * Outputs (fp32, overwritten): dx [T,d], dWg [d,E], dbg [E], dW1
+ * [E,d,d_ff], db1 [E,d_ff], dW2 [E,d_ff,d], db2 [E,d].
+ * Arithmetic: fp32 on the vector ALUs; bf16 operands are widened exactly;
+ * h is recomputed from x_perm, W1, b1 (rounded to the layer dtype, as the
+ * forward stores it).  ws: moe_backward_workspace_size bytes (its own
+ * workspace; the forward's may be read through x_perm / out_perm, so the
+ * two must not overlap). */
+size_t moe_backward_workspace_size(const moe_shape* s);
+int moe_layer_backward(const moe_shape* s, const void* x, const float* Wg, const void* W1, const float* b1,
+                       const void* W2, const float* dy, const int32_t* topk_idx, const float* topk_w,
+                       const int32_t* slot, const int32_t* offsets, const void* x_perm, const float* out_perm,
+                       float* dx, float* dWg, float* dbg, float* dW1, float* db1, float* dW2, float* db2,
+                       void* ws, size_t ws_bytes, void* stream);
+
 /* ---- measurement hook ------------------------------------------------------
  * Stages of moe_layer_forward, in launch order. */
 int moe_num_stages(void);

@@ -68,6 +68,8 @@ _sigs = {
     "moe_route_logits_ex": (C.c_int, [_SP, C.c_int, _P, _P, C.c_float, _P, _P, _P, _P]),
     "moe_aux_loss_ex": (C.c_int, [_SP, C.c_int, _P, _P, _P]),
     "moe_window_state_bytes": (C.c_size_t, [C.c_int64, C.c_int64]),
+    "moe_backward_workspace_size": (C.c_size_t, [_SP]),
+    "moe_layer_backward": (C.c_int, [_SP] + [_P] * 20 + [_Z, _P]),
     "moe_aux_loss_window": (C.c_int, [_SP, _P, _P, C.c_int64, _P, _P, _P]),
     "moe_layer_forward": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                     _P, _Z, _P]),
@@ -183,6 +185,27 @@ def moe_route_logits_ex(s, mode, logits, topk_idx, topk_w, noise=None, noise_sca
 
 def moe_aux_loss_ex(s, mode, load, aux, stream=None) -> None:
     _check(_lib.moe_aux_loss_ex(C.byref(s), int(mode), _ptr(load), _ptr(aux), _stream(stream)))
+
+
+def moe_backward_workspace_size(s: MoeShape) -> int:
+    return int(_lib.moe_backward_workspace_size(C.byref(s)))
+
+
+def backward_workspace(s: MoeShape, device="cuda"):
+    import torch
+    n = moe_backward_workspace_size(s)
+    if n == 0:
+        raise MoEError(2, _lib.moe_last_error().decode())
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def moe_layer_backward(s, x, Wg, W1, b1, W2, dy, topk_idx, topk_w, slot, offsets, x_perm, out_perm,
+                       dx, dWg, dbg, dW1, db1, dW2, db2, ws, stream=None) -> None:
+    _check(_lib.moe_layer_backward(C.byref(s), _ptr(x), _ptr(Wg), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(dy),
+                                   _ptr(topk_idx), _ptr(topk_w), _ptr(slot), _ptr(offsets), _ptr(x_perm),
+                                   _ptr(out_perm), _ptr(dx), _ptr(dWg), _ptr(dbg), _ptr(dW1), _ptr(db1),
+                                   _ptr(dW2), _ptr(db2), _ptr(ws), ws.numel() * ws.element_size(),
+                                   _stream(stream)))
 
 
 def moe_window_state_bytes(E: int, W: int) -> int:

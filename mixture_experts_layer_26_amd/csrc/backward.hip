@@ -1,0 +1,387 @@
+// backward.hip -- backward of the MoE layer forward (gfx950, fp32 vector ALUs).
+//
+// Gradients of sum(dy * y) with the forward's routing decisions (selection,
+// capacity, drops) fixed; they are piecewise constant.  [PithTrain] section
+// 4.1's layer is differentiated as autograd would: the combine y[t] +=
+// w[t,j] o[r], the expert FFN o = GELU(x W1 + b1) W2 + b2 and the gate
+// w = softmax(l_sel / tau), l = x Wg (+ bg).  Only experts that received rows
+// get weight gradients; the others are zero ([EP] section 4.3, expert-grained
+// gradients).
+//
+// Launch sequence (moe_layer_backward):
+//   1. combine_backward: per kept slot, dw[t,j] = dy[t] . o[r] and the
+//      expert-output gradient g[r] = w[t,j] dy[t] (fp32, packed rows);
+//   2. recompute per row a = x_perm W1 + b1 -> h = GELU(a), h' = GELU'(a);
+//   3. dh = g W2^T, da = dh * h'           (rows of each expert);
+//   4. dx_perm = da W1^T                   (rows of each expert);
+//   5. dW2[e] = h^T g, dW1[e] = x_perm^T da (sums over each expert's rows);
+//   6. db2[e], db1[e]: column sums of g and da over each expert's rows;
+//   7. gate: dl[t, idx_j] = w_j (dw_j - sum_i w_i dw_i) / tau, dWg = x^T dl,
+//      dbg = column sums of dl, dxg = dl Wg^T;
+//   8. dx[t] = sum_j dx_perm[slot[t,j]] + dxg[t].
+// The GEMMs (2-5, 7) are one tiled fp32 kernel, 64 x 64 outputs per
+// workgroup, 4 x 4 per thread, K in steps of 16 through LDS; bf16 operands
+// are widened exactly when staged.  Three operand patterns:
+//   NN: A rows of a segment, K-contiguous; B = W[e] [K][N]
+//   NT: A rows of a segment, K-contiguous; B = W[e] stored [N][K]
+//   TN: A and B both rows of a segment; K runs over the segment's rows
+#include "ffn_sched.h"
+#include "moe_kernels.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int BW_BM = 64, BW_BN = 64, BW_BK = 16, BW_THREADS = 256;
+constexpr int BW_PAD = 4;   // LDS row padding (floats)
+
+enum { BW_NN = 0, BW_NT = 1, BW_TN = 2 };
+enum { BWE_HGRAD = 0, BWE_DA = 1, BWE_STORE = 2, BWE_WGRAD = 3 };
+
+template <typename T>
+__device__ __forceinline__ float ld_elem(const T* p, int64_t i);
+template <>
+__device__ __forceinline__ float ld_elem<float>(const float* p, int64_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float ld_elem<uint16_t>(const uint16_t* p, int64_t i) { return bf16_bits_to_f32(p[i]); }
+
+template <typename T>
+__device__ __forceinline__ void st_elem(T* p, int64_t i, float v);
+template <>
+__device__ __forceinline__ void st_elem<float>(float* p, int64_t i, float v) { p[i] = v; }
+template <>
+__device__ __forceinline__ void st_elem<uint16_t>(uint16_t* p, int64_t i, float v) { p[i] = f32_to_bf16_bits(v); }
+
+// d/du [u Phi(u)] = Phi(u) + u phi(u), fp32 with the device library's erff
+__device__ __forceinline__ float gelu_grad(float u) {
+    return 0.5f * (1.0f + erff(u * 0.70710678118654752440f)) +
+           u * expf(-0.5f * u * u) * 0.39894228040143267794f;
+}
+
+}  // namespace
+
+// C[m][n] = sum_k A(m,k) B(k,n) for every item; see the header comment for
+// the operand patterns.  Row segments come from offsets[E+1] (or one segment
+// [0, M) when offsets is null).
+template <int MODE, int EPI, typename TA, typename TB, typename TH>
+__global__ __launch_bounds__(BW_THREADS) void bw_gemm_kernel(BwGemmArgs g) {
+    __shared__ __attribute__((aligned(16))) float As[BW_BK][BW_BM + BW_PAD];
+    __shared__ __attribute__((aligned(16))) float Bs[BW_BK][BW_BN + BW_PAD];
+    __shared__ int mt_pre[1025];
+    __shared__ int scan_tmp[32];
+    const int tid = threadIdx.x;
+    const int tx = tid & 15, ty = tid >> 4;   // 4 x 4 outputs: rows 4 ty.., cols 4 tx..
+    const int ntn = (g.N + BW_BN - 1) / BW_BN;
+    const TA* A = static_cast<const TA*>(g.A);
+    const TB* B = static_cast<const TB*>(g.B);
+
+    // ---- the item: expert e, rows [m0, m0 + mrows) or K range [k0, k1) ----
+    int e, m0, mrows, n0, kb, kend;
+    if constexpr (MODE == BW_TN) {
+        const int mtn = (g.M + BW_BM - 1) / BW_BM;
+        const int64_t item = blockIdx.x;
+        e = (int)(item / ((int64_t)mtn * ntn));
+        const int rest = (int)(item - (int64_t)e * mtn * ntn);
+        m0 = (rest / ntn) * BW_BM;
+        n0 = (rest % ntn) * BW_BN;
+        mrows = min(BW_BM, g.M - m0);
+        kb = g.offsets ? g.offsets[e] : 0;
+        kend = g.offsets ? g.offsets[e + 1] : g.K;
+    } else {
+        int total_mt;
+        if (g.offsets) {
+            total_mt = build_mtile_prefix(g.offsets, g.E, BW_BM, mt_pre, scan_tmp);
+        } else {
+            total_mt = (g.M + BW_BM - 1) / BW_BM;
+        }
+        if ((int64_t)blockIdx.x >= (int64_t)total_mt * ntn) return;
+        int mt, nt, seg0, seg1;
+        if (g.offsets) {
+            const WorkItem wi = decode_item(mt_pre, g.E, ntn, blockIdx.x);
+            e = wi.e;
+            mt = wi.mt;
+            nt = wi.nt;
+            seg0 = g.offsets[e];
+            seg1 = g.offsets[e + 1];
+        } else {
+            e = 0;
+            mt = blockIdx.x % total_mt;
+            nt = blockIdx.x / total_mt;
+            seg0 = 0;
+            seg1 = g.M;
+        }
+        m0 = seg0 + mt * BW_BM;
+        mrows = min(BW_BM, seg1 - m0);
+        n0 = nt * BW_BN;
+        kb = 0;
+        kend = g.K;
+    }
+    const int64_t bbase = (MODE == BW_TN) ? 0 : (int64_t)e * g.b_estride;
+
+    float acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+
+    // staging: each thread moves 4 elements of each 16 x 64 tile
+    for (int k0 = kb; k0 < kend; k0 += BW_BK) {
+        // A tile, As[k][m]
+        if constexpr (MODE == BW_TN) {
+            // A(m, k) = A[k lda + m]: 4 consecutive m at one k
+            const int kk = tid >> 4, mm = (tid & 15) * 4;
+            const int k = k0 + kk;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int m = m0 + mm + q;
+                As[kk][mm + q] = (k < kend && mm + q < mrows) ? ld_elem<TA>(A, (int64_t)k * g.lda + m) : 0.0f;
+            }
+        } else {
+            // A(m, k) = A[(m0 + m) lda + k]: 4 consecutive k of one row
+            const int mm = tid >> 2, kk = (tid & 3) * 4;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int k = k0 + kk + q;
+                As[kk + q][mm] = (mm < mrows && k < kend) ? ld_elem<TA>(A, (int64_t)(m0 + mm) * g.lda + k) : 0.0f;
+            }
+        }
+        // B tile, Bs[k][n]
+        if constexpr (MODE == BW_NT) {
+            // B(k, n) = B[e: n ldb + k]: 4 consecutive k of one column
+            const int nn = tid >> 2, kk = (tid & 3) * 4;
+            const int n = n0 + nn;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int k = k0 + kk + q;
+                Bs[kk + q][nn] = (n < g.N && k < kend) ? ld_elem<TB>(B, bbase + (int64_t)n * g.ldb + k) : 0.0f;
+            }
+        } else {
+            // NN: B(k, n) = B[e: k ldb + n]; TN: B[k ldb + n] (rows of the segment)
+            const int kk = tid >> 4, nn = (tid & 15) * 4;
+            const int k = k0 + kk;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int n = n0 + nn + q;
+                Bs[kk][nn + q] = (k < kend && n < g.N) ? ld_elem<TB>(B, bbase + (int64_t)k * g.ldb + n) : 0.0f;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < BW_BK; ++kk) {
+            const float4 a = *reinterpret_cast<const float4*>(&As[kk][ty * 4]);
+            const float4 b = *reinterpret_cast<const float4*>(&Bs[kk][tx * 4]);
+            const float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+
+    // ---- epilogue ----
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int m = ty * 4 + i;
+        if (m >= mrows) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int n = n0 + tx * 4 + j;
+            if (n >= g.N) continue;
+            float v = acc[i][j];
+            if constexpr (EPI == BWE_WGRAD) {
+                // dW[e][m0 + m][n]
+                static_cast<float*>(g.C)[(int64_t)e * g.M * g.N + (int64_t)(m0 + m) * g.N + n] = v;
+            } else {
+                const int64_t ci = (int64_t)(m0 + m) * g.N + n;
+                if constexpr (EPI == BWE_HGRAD) {
+                    v += g.bias[(int64_t)e * g.N + n];
+                    st_elem<TH>(static_cast<TH*>(g.C), ci, gelu_erf(v));
+                    g.C2[ci] = gelu_grad(v);
+                } else if constexpr (EPI == BWE_DA) {
+                    static_cast<float*>(g.C)[ci] = v * g.C2[ci];
+                } else {
+                    static_cast<float*>(g.C)[ci] = v;
+                }
+            }
+        }
+    }
+}
+
+// combine backward: per token, for each kept slot, dw = dy[t] . out[r] and
+// g[r] = w dy[t]; dropped slots get dw = 0
+__global__ __launch_bounds__(256) void combine_backward_kernel(int64_t T, int d, int k, const float* __restrict__ dy,
+                                                               const float* __restrict__ out,
+                                                               const int32_t* __restrict__ slot,
+                                                               const float* __restrict__ w, float* __restrict__ g,
+                                                               float* __restrict__ dw) {
+    __shared__ float part[256 / kWave];
+    const int64_t t = blockIdx.x;
+    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+    for (int j = 0; j < k; ++j) {
+        const int r = slot[t * k + j];
+        float s = 0.0f;
+        if (r >= 0) {
+            const float wt = w[t * k + j];
+            for (int c = threadIdx.x; c < d; c += blockDim.x) {
+                const float v = dy[t * d + c];
+                s = fmaf(v, out[(int64_t)r * d + c], s);
+                g[(int64_t)r * d + c] = wt * v;
+            }
+        }
+        s = wave_sum(s);
+        if (lane == 0) part[wid] = s;
+        __syncthreads();
+        if (threadIdx.x == 0) dw[t * k + j] = (r >= 0) ? (part[0] + part[1] + part[2] + part[3]) : 0.0f;
+        __syncthreads();
+    }
+}
+
+// column sums over row segments: out[e][c] = sum_{r in segment e} src[r][c]
+// (fp32, rows in order); one thread per (expert, column)
+__global__ __launch_bounds__(256) void segment_colsum_kernel(const float* __restrict__ src, const int32_t* offsets,
+                                                             int E, int64_t rows, int N, float* __restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (int64_t)E * N) return;
+    const int e = (int)(i / N), c = (int)(i - (int64_t)e * N);
+    const int r0 = offsets ? offsets[e] : 0, r1 = offsets ? offsets[e + 1] : (int)rows;
+    float s = 0.0f;
+    for (int r = r0; r < r1; ++r) s += src[(int64_t)r * N + c];
+    out[i] = s;
+}
+
+// gate softmax backward over the selected logits: one thread per token
+__global__ __launch_bounds__(256) void gate_backward_kernel(int64_t T, int E, int k, float tau,
+                                                            const int32_t* __restrict__ idx,
+                                                            const float* __restrict__ w,
+                                                            const float* __restrict__ dw, float* __restrict__ dl) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= T) return;
+    float s = 0.0f;
+    for (int j = 0; j < k; ++j) s = fmaf(w[t * k + j], dw[t * k + j], s);
+    for (int e = 0; e < E; ++e) dl[t * E + e] = 0.0f;
+    for (int j = 0; j < k; ++j) {
+        const int e = idx[t * k + j];
+        if ((unsigned)e < (unsigned)E) dl[t * E + e] = w[t * k + j] * (dw[t * k + j] - s) / tau;
+    }
+}
+
+// dx[t] = sum_j dx_perm[slot[t,j]] (j order) + dxg[t]
+__global__ __launch_bounds__(256) void dispatch_backward_kernel(int64_t T, int d, int k,
+                                                                const float* __restrict__ dxp,
+                                                                const int32_t* __restrict__ slot,
+                                                                const float* __restrict__ dxg,
+                                                                float* __restrict__ dx) {
+    const int64_t t = blockIdx.x;
+    for (int c = threadIdx.x; c < d; c += blockDim.x) {
+        float s = 0.0f;
+        for (int j = 0; j < k; ++j) {
+            const int r = slot[t * k + j];
+            if (r >= 0) s += dxp[(int64_t)r * d + c];
+        }
+        dx[t * d + c] = s + dxg[t * d + c];
+    }
+}
+
+// ---- host ------------------------------------------------------------------
+
+template <int MODE, int EPI, typename TA, typename TB, typename TH>
+static hipError_t bw_launch(const BwGemmArgs& g, int64_t max_rows, hipStream_t st) {
+    const int ntn = (g.N + BW_BN - 1) / BW_BN;
+    int64_t blocks;
+    if (MODE == BW_TN) blocks = (int64_t)g.E * ((g.M + BW_BM - 1) / BW_BM) * ntn;
+    else if (g.offsets) blocks = ((max_rows + BW_BM - 1) / BW_BM + g.E) * ntn;   // bound; extra blocks exit
+    else blocks = (int64_t)((g.M + BW_BM - 1) / BW_BM) * ntn;
+    if (blocks < 1) return hipSuccess;
+    hipLaunchKernelGGL((bw_gemm_kernel<MODE, EPI, TA, TB, TH>), dim3((unsigned)blocks), dim3(BW_THREADS), 0, st, g);
+    return hipGetLastError();
+}
+
+#define BW_CHECK(x)                                  \
+    do {                                             \
+        hipError_t e_ = (x);                         \
+        if (e_ != hipSuccess) return e_;             \
+    } while (0)
+
+template <typename ET>
+static hipError_t layer_backward_t(const BackwardArgs& b, hipStream_t st) {
+    const int64_t T = b.T;
+    const int d = b.d, E = b.E, k = b.k, F = b.dff;
+    // 1. combine backward
+    hipLaunchKernelGGL(combine_backward_kernel, dim3((unsigned)T), dim3(256), 0, st, T, d, k, b.dy, b.out_perm,
+                       b.slot, b.topk_w, b.g, b.dw);
+    BW_CHECK(hipGetLastError());
+    // 2. recompute h and GELU'(a) per row
+    BwGemmArgs g{};
+    g.A = b.x_perm; g.lda = d;
+    g.B = b.W1; g.ldb = F; g.b_estride = (int64_t)d * F;
+    g.offsets = b.offsets; g.E = E; g.K = d; g.N = F;
+    g.bias = b.b1; g.C = b.h; g.C2 = b.hgrad;
+    BW_CHECK((bw_launch<BW_NN, BWE_HGRAD, ET, ET, ET>(g, b.max_rows, st)));
+    // 3. dh = g W2^T (W2[e] stored [F][d] = [N][K]), da = dh * GELU'(a)
+    g = BwGemmArgs{};
+    g.A = b.g; g.lda = d;
+    g.B = b.W2; g.ldb = d; g.b_estride = (int64_t)F * d;
+    g.offsets = b.offsets; g.E = E; g.K = d; g.N = F;
+    g.C = b.da; g.C2 = b.hgrad;
+    BW_CHECK((bw_launch<BW_NT, BWE_DA, float, ET, float>(g, b.max_rows, st)));
+    // 4. dx_perm = da W1^T (W1[e] stored [d][F] = [N][K])
+    g = BwGemmArgs{};
+    g.A = b.da; g.lda = F;
+    g.B = b.W1; g.ldb = F; g.b_estride = (int64_t)d * F;
+    g.offsets = b.offsets; g.E = E; g.K = F; g.N = d;
+    g.C = b.dx_perm;
+    BW_CHECK((bw_launch<BW_NT, BWE_STORE, float, ET, float>(g, b.max_rows, st)));
+    // 5. dW2[e] = h^T g  ([F][d]), dW1[e] = x_perm^T da  ([d][F])
+    g = BwGemmArgs{};
+    g.A = b.h; g.lda = F;
+    g.B = b.g; g.ldb = d;
+    g.offsets = b.offsets; g.E = E; g.M = F; g.N = d;
+    g.C = b.dW2;
+    BW_CHECK((bw_launch<BW_TN, BWE_WGRAD, ET, float, float>(g, b.max_rows, st)));
+    g = BwGemmArgs{};
+    g.A = b.x_perm; g.lda = d;
+    g.B = b.da; g.ldb = F;
+    g.offsets = b.offsets; g.E = E; g.M = d; g.N = F;
+    g.C = b.dW1;
+    BW_CHECK((bw_launch<BW_TN, BWE_WGRAD, ET, float, float>(g, b.max_rows, st)));
+    // 6. bias gradients
+    {
+        const int64_t n2 = (int64_t)E * d, n1 = (int64_t)E * F;
+        hipLaunchKernelGGL(segment_colsum_kernel, dim3((unsigned)((n2 + 255) / 256)), dim3(256), 0, st, b.g,
+                           b.offsets, E, (int64_t)0, d, b.db2);
+        BW_CHECK(hipGetLastError());
+        hipLaunchKernelGGL(segment_colsum_kernel, dim3((unsigned)((n1 + 255) / 256)), dim3(256), 0, st, b.da,
+                           b.offsets, E, (int64_t)0, F, b.db1);
+        BW_CHECK(hipGetLastError());
+    }
+    // 7. gate
+    hipLaunchKernelGGL(gate_backward_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, st, T, E, k, b.tau,
+                       b.topk_idx, b.topk_w, b.dw, b.dl);
+    BW_CHECK(hipGetLastError());
+    g = BwGemmArgs{};
+    g.A = b.x; g.lda = d;
+    g.B = b.dl; g.ldb = E;
+    g.E = 1; g.M = d; g.N = E; g.K = (int)T;
+    g.C = b.dWg;
+    BW_CHECK((bw_launch<BW_TN, BWE_WGRAD, ET, float, float>(g, b.max_rows, st)));
+    hipLaunchKernelGGL(segment_colsum_kernel, dim3((unsigned)((E + 255) / 256)), dim3(256), 0, st, b.dl,
+                       (const int32_t*)nullptr, 1, T, E, b.dbg);
+    BW_CHECK(hipGetLastError());
+    g = BwGemmArgs{};
+    g.A = b.dl; g.lda = E;
+    g.B = b.Wg; g.ldb = E;   // Wg [d][E] = [N][K]
+    g.E = 1; g.M = (int)T; g.K = E; g.N = d;
+    g.C = b.dxg;
+    BW_CHECK((bw_launch<BW_NT, BWE_STORE, float, float, float>(g, b.max_rows, st)));
+    // 8. dx
+    hipLaunchKernelGGL(dispatch_backward_kernel, dim3((unsigned)T), dim3(256), 0, st, T, d, k, b.dx_perm, b.slot,
+                       b.dxg, b.dx);
+    return hipGetLastError();
+}
+
+hipError_t launch_layer_backward(const BackwardArgs& b, int dtype, hipStream_t st) {
+    return dtype == MOE_BF16 ? layer_backward_t<uint16_t>(b, st) : layer_backward_t<float>(b, st);
+}
+
+}  // namespace moe

@@ -429,6 +429,92 @@ int moe_aux_loss_ex(const moe_shape* s, int mode, const int32_t* load, float* au
     return MOE_OK;
 }
 
+struct BwLayout {
+    size_t g, h, hgrad, da, dx_perm, dw, dl, dxg, total;
+};
+
+static BwLayout bw_layout(const Geo& g) {
+    BwLayout L{};
+    size_t p = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = p;
+        p = align_up(p + (bytes ? bytes : 1));
+        return at;
+    };
+    const size_t R = (size_t)g.max_rows;
+    L.g = take(4 * R * g.d);
+    L.h = take((size_t)g.esz * R * g.dff);
+    L.hgrad = take(4 * R * g.dff);
+    L.da = take(4 * R * g.dff);
+    L.dx_perm = take(4 * R * g.d);
+    L.dw = take(4 * (size_t)(g.T * g.k));
+    L.dl = take(4 * (size_t)(g.T * g.E));
+    L.dxg = take(4 * (size_t)(g.T * g.d));
+    L.total = p;
+    return L;
+}
+
+size_t moe_backward_workspace_size(const moe_shape* s) {
+    Geo g;
+    if (validate(s, &g)) return 0;
+    return bw_layout(g).total;
+}
+
+int moe_layer_backward(const moe_shape* s, const void* x, const float* Wg, const void* W1, const float* b1,
+                       const void* W2, const float* dy, const int32_t* topk_idx, const float* topk_w,
+                       const int32_t* slot, const int32_t* offsets, const void* x_perm, const float* out_perm,
+                       float* dx, float* dWg, float* dbg, float* dW1, float* db1, float* dW2, float* db2, void* ws,
+                       size_t ws_bytes, void* stream) {
+    Geo g;
+    if (int rc = validate(s, &g)) return rc;
+    MOE_REQUIRE(x);
+    MOE_REQUIRE(Wg);
+    MOE_REQUIRE(W1);
+    MOE_REQUIRE(b1);
+    MOE_REQUIRE(W2);
+    MOE_REQUIRE(dy);
+    MOE_REQUIRE(topk_idx);
+    MOE_REQUIRE(topk_w);
+    MOE_REQUIRE(slot);
+    MOE_REQUIRE(offsets);
+    MOE_REQUIRE(x_perm);
+    MOE_REQUIRE(out_perm);
+    MOE_REQUIRE(dx);
+    MOE_REQUIRE(dWg);
+    MOE_REQUIRE(dbg);
+    MOE_REQUIRE(dW1);
+    MOE_REQUIRE(db1);
+    MOE_REQUIRE(dW2);
+    MOE_REQUIRE(db2);
+    const BwLayout L = bw_layout(g);
+    if (ws == nullptr) return fail(MOE_ERR_WORKSPACE, "workspace is NULL");
+    if (misaligned(ws)) return fail(MOE_ERR_ALIGN, "workspace is not 16-byte aligned");
+    if (ws_bytes < L.total) return fail(MOE_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, L.total);
+    BackwardArgs b{};
+    b.T = g.T;
+    b.max_rows = g.max_rows;
+    b.d = (int)g.d;
+    b.E = (int)g.E;
+    b.k = (int)g.k;
+    b.dff = (int)g.dff;
+    b.tau = s->temperature;
+    b.x = x; b.Wg = Wg; b.W1 = W1; b.b1 = b1; b.W2 = W2;
+    b.dy = dy; b.topk_idx = topk_idx; b.topk_w = topk_w; b.slot = slot; b.offsets = offsets;
+    b.x_perm = x_perm; b.out_perm = out_perm;
+    b.dx = dx; b.dWg = dWg; b.dbg = dbg; b.dW1 = dW1; b.db1 = db1; b.dW2 = dW2; b.db2 = db2;
+    b.g = at<float>(ws, L.g);
+    b.h = at<void>(ws, L.h);
+    b.hgrad = at<float>(ws, L.hgrad);
+    b.da = at<float>(ws, L.da);
+    b.dx_perm = at<float>(ws, L.dx_perm);
+    b.dw = at<float>(ws, L.dw);
+    b.dl = at<float>(ws, L.dl);
+    b.dxg = at<float>(ws, L.dxg);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    MOE_HIP(launch_layer_backward(b, s->dtype, st), "backward kernel launch");
+    return MOE_OK;
+}
+
 size_t moe_window_state_bytes(int64_t E, int64_t W) {
     if (E < 1 || E > 1024 || W < 1 || W > (int64_t(1) << 20)) return 0;
     return window_state_bytes(E, W);

@@ -92,6 +92,38 @@ size_t window_state_bytes(int64_t E, int64_t W);
 hipError_t launch_window_aux(int E, int64_t W, int64_t T, int k, float lambda, const int32_t* counts, void* state,
                              float* aux, float* pbar, hipStream_t st);
 
+// ---- backward.hip: the layer backward ------------------------------------
+struct BwGemmArgs {
+    const void* A;           // see backward.hip for the three operand patterns
+    const void* B;
+    int64_t lda, ldb;
+    int64_t b_estride;       // elements between experts' weight matrices (NN, NT)
+    const int32_t* offsets;  // row segments [E+1], or null: one segment
+    int E, M, N, K;
+    const float* bias;       // NN recompute: b1 [E, N]
+    void* C;                 // output
+    float* C2;               // NN: GELU'(a) out; NT with GELU' product: GELU'(a) in
+};
+struct BackwardArgs {
+    int64_t T, max_rows;
+    int d, E, k, dff;
+    float tau;
+    const void* x; const float* Wg; const void* W1; const float* b1; const void* W2;
+    const float* dy; const int32_t* topk_idx; const float* topk_w; const int32_t* slot;
+    const int32_t* offsets; const void* x_perm; const float* out_perm;
+    float *dx, *dWg, *dbg, *dW1, *db1, *dW2, *db2;
+    // workspace
+    float* g;        // [max_rows, d] expert-output gradients
+    void* h;         // [max_rows, dff] recomputed GELU(a), layer dtype
+    float* hgrad;    // [max_rows, dff] GELU'(a)
+    float* da;       // [max_rows, dff]
+    float* dx_perm;  // [max_rows, d]
+    float* dw;       // [T, k]
+    float* dl;       // [T, E]
+    float* dxg;      // [T, d]
+};
+hipError_t launch_layer_backward(const BackwardArgs& b, int dtype, hipStream_t st);
+
 // device properties (moe_api.hip)
 int device_cu_count();
 

@@ -156,3 +156,22 @@ def test_router_variant_and_loss_validation(moe):
     with pytest.raises(moe.MoEError) as ei:
         moe.moe_coactivation(s1, p, None, p, stream=0)
     assert ei.value.status == 1
+
+
+def _declared_param_counts():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    out = {}
+    for m in re.finditer(r"(moe_\w+)\s*\(([^)]*)\)\s*;", src):
+        params = m.group(2).strip()
+        out[m.group(1)] = 0 if params in ("", "void") else params.count(",") + 1
+    return out
+
+
+def test_binding_signatures_match_header(moe):
+    """Every ctypes signature of the binding has as many parameters as the
+    header declares (a short list shifts the trailing arguments)."""
+    counts = _declared_param_counts()
+    for name, (_, args) in moe._sigs.items():
+        assert name in counts, name
+        assert len(args) == counts[name], (name, len(args), counts[name])
