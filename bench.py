@@ -64,6 +64,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the oracle's expert-FFN sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -273,6 +274,46 @@ def time_router_variant(moe, s, cfg, d, ws, stream):
             "variance_loss_us": us_loss, "variance_loss": float(aux.cpu().numpy()[0])}
 
 
+def time_backward(moe, s, cfg, d, ws, stream, reps=5):
+    """moe_layer_backward after one forward of the same batch (dy seeded
+    N(0,1)); HIP events around each call.  FLOPs: five GEMMs of 2 S d d_ff
+    each (recompute, dh, dx_perm, dW1, dW2) plus the gate's two of 2 T d E."""
+    import numpy as np
+    import torch
+    dev = d["x"].device
+    T, E, k, D, F = cfg.T, cfg.E, cfg.k, cfg.d, cfg.d_ff
+    f32, i32 = torch.float32, torch.int32
+    y, counts, aux = (torch.empty((T, D), dtype=f32, device=dev), torch.empty(E, dtype=i32, device=dev),
+                      torch.empty(1, dtype=f32, device=dev))
+    idx, w = torch.empty((T, k), dtype=i32, device=dev), torch.empty((T, k), dtype=f32, device=dev)
+    moe.moe_layer_forward(s, d["x"], d["Wg"], d["bg"], d["W1"], d["b1"], d["W2"], d["b2"], y, counts, aux, ws,
+                          topk_idx=idx, topk_w=w, stream=stream)
+    R = moe.moe_max_rows(s)
+
+    def region(which, dtype, n, esz):
+        off = moe.moe_workspace_offset(s, which)
+        return ws[off:off + n * esz].view(dtype)
+
+    slot = region(moe.MOE_WS_SLOT, i32, T * k, 4)
+    offsets = region(moe.MOE_WS_OFFSETS, i32, E + 1, 4)
+    xperm = region(moe.MOE_WS_XPERM, torch.int16 if cfg.dtype == "bf16" else f32, R * D,
+                   2 if cfg.dtype == "bf16" else 4)
+    outp = region(moe.MOE_WS_OUT, f32, R * D, 4)
+    dy = torch.from_numpy(np.random.default_rng(77).standard_normal((T, D)).astype(np.float32)).to(dev)
+    g = [torch.empty(sh, dtype=f32, device=dev) for sh in ((T, D), (D, E), (E,), (E, D, F), (E, F), (E, F, D), (E, D))]
+    bws = moe.backward_workspace(s, dev)
+    us = _median_us(lambda: moe.moe_layer_backward(s, d["x"], d["Wg"], d["W1"], d["b1"], d["W2"], dy, idx, w, slot,
+                                                   offsets, xperm, outp, *g, bws, stream=stream), stream, reps)
+    S = int(counts.cpu().numpy().sum())
+    flops = 10 * S * D * F + 4 * T * D * E
+    bf16 = cfg.dtype == "bf16"
+    peak = PEAK_BF16 if bf16 else PEAK_FP32
+    return {"ms": us / 1e3, "tflops": flops / (us * 1e-6) / 1e12, "flops": flops,
+            "peak_tflops": peak / 1e12, "frac_peak": flops / (us * 1e-6) / peak,
+            "arith": ("expert GEMMs on bf16 MFMA (fp32 accumulate), gate GEMMs on fp32 vector ALUs" if bf16
+                      else "fp32 vector ALUs")}
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -398,6 +439,8 @@ def main():
     }
     out["heat_map"] = time_heat_map(moe, s, cfg, d, y, counts, aux, ws, stream)
     out["router_variant"] = time_router_variant(moe, s, cfg, d, ws, stream)
+    if not args.no_backward:
+        out["backward"] = time_backward(moe, s, cfg, d, ws, stream)
     if args.copy_calib:
         src = torch.empty(COPY_CALIB_BYTES, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

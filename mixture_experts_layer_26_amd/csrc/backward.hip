@@ -19,14 +19,18 @@
 //   7. gate: dl[t, idx_j] = w_j (dw_j - sum_i w_i dw_i) / tau, dWg = x^T dl,
 //      dbg = column sums of dl, dxg = dl Wg^T;
 //   8. dx[t] = sum_j dx_perm[slot[t,j]] + dxg[t].
-// The GEMMs (2-5, 7) are one tiled fp32 kernel, 64 x 64 outputs per
-// workgroup, 4 x 4 per thread, K in steps of 16 through LDS; bf16 operands
-// are widened exactly when staged.  Three operand patterns:
+// The fp32 GEMMs (fp32 layers, and the gate) are one tiled kernel on the
+// vector ALUs, 64 x 64 outputs per workgroup, 4 x 4 per thread, K in steps
+// of 16 through LDS (bf16 operands widened exactly when staged); the expert
+// GEMMs of bf16 layers run on the matrix cores (bw_mfma_kernel).  Three
+// operand patterns:
 //   NN: A rows of a segment, K-contiguous; B = W[e] [K][N]
 //   NT: A rows of a segment, K-contiguous; B = W[e] stored [N][K]
 //   TN: A and B both rows of a segment; K runs over the segment's rows
 #include "ffn_sched.h"
 #include "moe_kernels.h"
+
+#include <type_traits>
 
 namespace moe {
 
@@ -208,12 +212,178 @@ __global__ __launch_bounds__(BW_THREADS) void bw_gemm_kernel(BwGemmArgs g) {
     }
 }
 
+// bf16 layers: the same three patterns on v_mfma_f32_16x16x32_bf16, 128 x
+// 128 outputs per workgroup (four waves of 64 x 64), K in steps of 32.  Both
+// LDS tiles hold their operand K-contiguous ([row][k], rows padded to 40
+// elements so the 16 rows a fragment read touches fall on disjoint banks);
+// a K-contiguous global operand is staged with 16-byte loads and stores, an
+// M/N-contiguous one (the weight W1 of the recompute, both operands of the
+// weight gradients) with 16-byte loads and 2-byte transposing stores.  The
+// next K-step's global loads are in flight during the current MFMAs.
+constexpr int BWM_BM = 128, BWM_BN = 128, BWM_BK = 32, BWM_LDK = BWM_BK + 8;
+
+template <bool KC>   // KC: the operand is K-contiguous in global memory
+__device__ __forceinline__ void bwm_load(const uint16_t* p, int64_t ld, int r0, int rlim, int k0, int kend, int tid,
+                                         uint4 (&reg)[2]) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int c = tid + 256 * q;
+        if constexpr (KC) {
+            const int r = c >> 2, kc = (c & 3) * 8;
+            reg[q] = (r < rlim && k0 + kc < kend)
+                         ? *reinterpret_cast<const uint4*>(p + (int64_t)(r0 + r) * ld + k0 + kc)
+                         : make_uint4(0u, 0u, 0u, 0u);
+        } else {
+            const int k = c >> 4, rc = (c & 15) * 8;
+            reg[q] = (k0 + k < kend && rc < rlim) ? *reinterpret_cast<const uint4*>(p + (int64_t)(k0 + k) * ld + r0 + rc)
+                                                  : make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
+}
+
+template <bool KC>
+__device__ __forceinline__ void bwm_store(uint16_t* s, int tid, const uint4 (&reg)[2]) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int c = tid + 256 * q;
+        if constexpr (KC) {
+            const int r = c >> 2, kc = (c & 3) * 8;
+            *reinterpret_cast<uint4*>(s + r * BWM_LDK + kc) = reg[q];
+        } else {
+            const int k = c >> 4, rc = (c & 15) * 8;
+            const uint32_t w[4] = {reg[q].x, reg[q].y, reg[q].z, reg[q].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                s[(rc + 2 * i) * BWM_LDK + k] = (uint16_t)(w[i] & 0xffffu);
+                s[(rc + 2 * i + 1) * BWM_LDK + k] = (uint16_t)(w[i] >> 16);
+            }
+        }
+    }
+}
+
+template <int MODE, int EPI>
+__global__ __launch_bounds__(256) void bw_mfma_kernel(BwGemmArgs g) {
+    __shared__ __attribute__((aligned(16))) uint16_t As[BWM_BM * BWM_LDK];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[BWM_BN * BWM_LDK];
+    __shared__ int mt_pre[1025];
+    __shared__ int scan_tmp[32];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+    const int wm = wid >> 1, wn = wid & 1;
+    const int ntn = (g.N + BWM_BN - 1) / BWM_BN;
+    const uint16_t* A = static_cast<const uint16_t*>(g.A);
+    const uint16_t* B = static_cast<const uint16_t*>(g.B);
+
+    int e, m0, mrows, n0, kb, kend;
+    if constexpr (MODE == BW_TN) {
+        const int mtn = (g.M + BWM_BM - 1) / BWM_BM;
+        const int64_t item = blockIdx.x;
+        e = (int)(item / ((int64_t)mtn * ntn));
+        const int rest = (int)(item - (int64_t)e * mtn * ntn);
+        m0 = (rest / ntn) * BWM_BM;
+        n0 = (rest % ntn) * BWM_BN;
+        mrows = min(BWM_BM, g.M - m0);
+        kb = g.offsets[e];
+        kend = g.offsets[e + 1];
+    } else {
+        const int total_mt = build_mtile_prefix(g.offsets, g.E, BWM_BM, mt_pre, scan_tmp);
+        if ((int64_t)blockIdx.x >= (int64_t)total_mt * ntn) return;
+        const WorkItem wi = decode_item(mt_pre, g.E, ntn, blockIdx.x);
+        e = wi.e;
+        m0 = g.offsets[e] + wi.mt * BWM_BM;
+        mrows = min(BWM_BM, g.offsets[e + 1] - m0);
+        n0 = wi.nt * BWM_BN;
+        kb = 0;
+        kend = g.K;
+    }
+    const int nrows = min(BWM_BN, g.N - n0);
+    const uint16_t* Bb = B + ((MODE == BW_TN) ? 0 : (int64_t)e * g.b_estride);
+
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // A: rows of the segment (K-contiguous) or, for TN, rows k of the segment
+    // holding M-contiguous values; B likewise
+    constexpr bool AKC = MODE != BW_TN, BKC = MODE == BW_NT;
+    uint4 ra[2], rb[2];
+    auto load = [&](int k0) {
+        if constexpr (AKC) bwm_load<true>(A, g.lda, m0, mrows, k0, kend, tid, ra);
+        else bwm_load<false>(A, g.lda, m0, mrows, k0, kend, tid, ra);
+        if constexpr (BKC) bwm_load<true>(Bb, g.ldb, n0, nrows, k0, kend, tid, rb);
+        else bwm_load<false>(Bb, g.ldb, n0, nrows, k0, kend, tid, rb);
+    };
+    if (kb < kend) load(kb);
+    for (int k0 = kb; k0 < kend; k0 += BWM_BK) {
+        __syncthreads();   // the previous step's fragment reads are done
+        bwm_store<AKC>(As, tid, ra);
+        bwm_store<BKC>(Bs, tid, rb);
+        __syncthreads();
+        if (k0 + BWM_BK < kend) load(k0 + BWM_BK);
+        bf16x8_t af[4], bfr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            af[i] = *reinterpret_cast<const bf16x8_t*>(&As[(wm * 64 + i * 16 + (lane & 15)) * BWM_LDK + 8 * (lane >> 4)]);
+            bfr[i] = *reinterpret_cast<const bf16x8_t*>(&Bs[(wn * 64 + i * 16 + (lane & 15)) * BWM_LDK + 8 * (lane >> 4)]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+    }
+
+    // lane l of block [i][j]: row 16 i + l % 16, columns 16 j + 4 (l / 16)..+3
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int m = wm * 64 + i * 16 + (lane & 15);
+        if (m >= mrows) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int n = n0 + wn * 64 + j * 16 + 4 * (lane >> 4);
+            if (n >= g.N) continue;
+            f32x4_t v = acc[i][j];
+            if constexpr (EPI == BWE_WGRAD) {
+                *reinterpret_cast<f32x4_t*>(static_cast<float*>(g.C) + (int64_t)e * g.M * g.N +
+                                            (int64_t)(m0 + m) * g.N + n) = v;
+            } else {
+                const int64_t ci = (int64_t)(m0 + m) * g.N + n;
+                if constexpr (EPI == BWE_HGRAD) {
+                    const f32x4_t bb = *reinterpret_cast<const f32x4_t*>(g.bias + (int64_t)e * g.N + n);
+                    v += bb;
+                    uint16_t hb[4];
+                    f32x4_t gr;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        hb[q] = f32_to_bf16_bits(gelu_erf(v[q]));
+                        gr[q] = gelu_grad(v[q]);
+                    }
+                    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(g.C) + ci) =
+                        make_uint2(hb[0] | ((uint32_t)hb[1] << 16), hb[2] | ((uint32_t)hb[3] << 16));
+                    *reinterpret_cast<f32x4_t*>(g.C2 + ci) = gr;
+                } else if constexpr (EPI == BWE_DA) {
+                    const f32x4_t gr = *reinterpret_cast<const f32x4_t*>(g.C2 + ci);
+                    v *= gr;
+                    const uint16_t d0 = f32_to_bf16_bits(v[0]), d1 = f32_to_bf16_bits(v[1]);
+                    const uint16_t d2 = f32_to_bf16_bits(v[2]), d3 = f32_to_bf16_bits(v[3]);
+                    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(g.C) + ci) =
+                        make_uint2(d0 | ((uint32_t)d1 << 16), d2 | ((uint32_t)d3 << 16));
+                } else {
+                    *reinterpret_cast<f32x4_t*>(static_cast<float*>(g.C) + ci) = v;
+                }
+            }
+        }
+    }
+}
+
 // combine backward: per token, for each kept slot, dw = dy[t] . out[r] and
 // g[r] = w dy[t]; dropped slots get dw = 0
+template <typename TG>
 __global__ __launch_bounds__(256) void combine_backward_kernel(int64_t T, int d, int k, const float* __restrict__ dy,
                                                                const float* __restrict__ out,
                                                                const int32_t* __restrict__ slot,
-                                                               const float* __restrict__ w, float* __restrict__ g,
+                                                               const float* __restrict__ w, TG* __restrict__ g,
                                                                float* __restrict__ dw) {
     __shared__ float part[256 / kWave];
     const int64_t t = blockIdx.x;
@@ -226,7 +396,7 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(int64_t T, int d,
             for (int c = threadIdx.x; c < d; c += blockDim.x) {
                 const float v = dy[t * d + c];
                 s = fmaf(v, out[(int64_t)r * d + c], s);
-                g[(int64_t)r * d + c] = wt * v;
+                st_elem<TG>(g, (int64_t)r * d + c, wt * v);
             }
         }
         s = wave_sum(s);
@@ -239,14 +409,15 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(int64_t T, int d,
 
 // column sums over row segments: out[e][c] = sum_{r in segment e} src[r][c]
 // (fp32, rows in order); one thread per (expert, column)
-__global__ __launch_bounds__(256) void segment_colsum_kernel(const float* __restrict__ src, const int32_t* offsets,
+template <typename TS>
+__global__ __launch_bounds__(256) void segment_colsum_kernel(const TS* __restrict__ src, const int32_t* offsets,
                                                              int E, int64_t rows, int N, float* __restrict__ out) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= (int64_t)E * N) return;
     const int e = (int)(i / N), c = (int)(i - (int64_t)e * N);
     const int r0 = offsets ? offsets[e] : 0, r1 = offsets ? offsets[e + 1] : (int)rows;
     float s = 0.0f;
-    for (int r = r0; r < r1; ++r) s += src[(int64_t)r * N + c];
+    for (int r = r0; r < r1; ++r) s += ld_elem<TS>(src, (int64_t)r * N + c);
     out[i] = s;
 }
 
@@ -303,69 +474,98 @@ static hipError_t bw_launch(const BwGemmArgs& g, int64_t max_rows, hipStream_t s
         if (e_ != hipSuccess) return e_;             \
     } while (0)
 
+template <int MODE, int EPI>
+static hipError_t bwm_launch(const BwGemmArgs& g, int64_t max_rows, hipStream_t st) {
+    const int ntn = (g.N + BWM_BN - 1) / BWM_BN;
+    const int64_t blocks = (MODE == BW_TN) ? (int64_t)g.E * ((g.M + BWM_BM - 1) / BWM_BM) * ntn
+                                           : ((max_rows + BWM_BM - 1) / BWM_BM + g.E) * ntn;   // bound
+    if (blocks < 1) return hipSuccess;
+    hipLaunchKernelGGL((bw_mfma_kernel<MODE, EPI>), dim3((unsigned)blocks), dim3(256), 0, st, g);
+    return hipGetLastError();
+}
+
+// steps 2-5: the expert FFN backward.  bf16 layers: matrix cores, with the
+// expert-output gradient g and da held in bf16 as GEMM operands; fp32
+// layers: vector ALUs in fp32 throughout.
 template <typename ET>
-static hipError_t layer_backward_t(const BackwardArgs& b, hipStream_t st) {
-    const int64_t T = b.T;
-    const int d = b.d, E = b.E, k = b.k, F = b.dff;
-    // 1. combine backward
-    hipLaunchKernelGGL(combine_backward_kernel, dim3((unsigned)T), dim3(256), 0, st, T, d, k, b.dy, b.out_perm,
-                       b.slot, b.topk_w, b.g, b.dw);
-    BW_CHECK(hipGetLastError());
-    // 2. recompute h and GELU'(a) per row
+static hipError_t ffn_backward_t(const BackwardArgs& b, hipStream_t st) {
+    const int d = b.d, E = b.E, F = b.dff;
+    constexpr bool kMfma = sizeof(ET) == 2;
     BwGemmArgs g{};
+    // 2. recompute h and GELU'(a): x_perm W1[e] + b1[e]
     g.A = b.x_perm; g.lda = d;
     g.B = b.W1; g.ldb = F; g.b_estride = (int64_t)d * F;
     g.offsets = b.offsets; g.E = E; g.K = d; g.N = F;
     g.bias = b.b1; g.C = b.h; g.C2 = b.hgrad;
-    BW_CHECK((bw_launch<BW_NN, BWE_HGRAD, ET, ET, ET>(g, b.max_rows, st)));
-    // 3. dh = g W2^T (W2[e] stored [F][d] = [N][K]), da = dh * GELU'(a)
+    if constexpr (kMfma) BW_CHECK((bwm_launch<BW_NN, BWE_HGRAD>(g, b.max_rows, st)));
+    else BW_CHECK((bw_launch<BW_NN, BWE_HGRAD, ET, ET, ET>(g, b.max_rows, st)));
+    // 3. dh = g W2[e]^T (W2[e] stored [F][d] = [N][K]), da = dh * GELU'(a)
     g = BwGemmArgs{};
     g.A = b.g; g.lda = d;
     g.B = b.W2; g.ldb = d; g.b_estride = (int64_t)F * d;
     g.offsets = b.offsets; g.E = E; g.K = d; g.N = F;
     g.C = b.da; g.C2 = b.hgrad;
-    BW_CHECK((bw_launch<BW_NT, BWE_DA, float, ET, float>(g, b.max_rows, st)));
-    // 4. dx_perm = da W1^T (W1[e] stored [d][F] = [N][K])
+    if constexpr (kMfma) BW_CHECK((bwm_launch<BW_NT, BWE_DA>(g, b.max_rows, st)));
+    else BW_CHECK((bw_launch<BW_NT, BWE_DA, float, ET, float>(g, b.max_rows, st)));
+    // 4. dx_perm = da W1[e]^T (W1[e] stored [d][F] = [N][K])
     g = BwGemmArgs{};
     g.A = b.da; g.lda = F;
     g.B = b.W1; g.ldb = F; g.b_estride = (int64_t)d * F;
     g.offsets = b.offsets; g.E = E; g.K = F; g.N = d;
     g.C = b.dx_perm;
-    BW_CHECK((bw_launch<BW_NT, BWE_STORE, float, ET, float>(g, b.max_rows, st)));
+    if constexpr (kMfma) BW_CHECK((bwm_launch<BW_NT, BWE_STORE>(g, b.max_rows, st)));
+    else BW_CHECK((bw_launch<BW_NT, BWE_STORE, float, ET, float>(g, b.max_rows, st)));
     // 5. dW2[e] = h^T g  ([F][d]), dW1[e] = x_perm^T da  ([d][F])
     g = BwGemmArgs{};
     g.A = b.h; g.lda = F;
     g.B = b.g; g.ldb = d;
     g.offsets = b.offsets; g.E = E; g.M = F; g.N = d;
     g.C = b.dW2;
-    BW_CHECK((bw_launch<BW_TN, BWE_WGRAD, ET, float, float>(g, b.max_rows, st)));
+    if constexpr (kMfma) BW_CHECK((bwm_launch<BW_TN, BWE_WGRAD>(g, b.max_rows, st)));
+    else BW_CHECK((bw_launch<BW_TN, BWE_WGRAD, ET, float, float>(g, b.max_rows, st)));
     g = BwGemmArgs{};
     g.A = b.x_perm; g.lda = d;
     g.B = b.da; g.ldb = F;
     g.offsets = b.offsets; g.E = E; g.M = d; g.N = F;
     g.C = b.dW1;
-    BW_CHECK((bw_launch<BW_TN, BWE_WGRAD, ET, float, float>(g, b.max_rows, st)));
+    if constexpr (kMfma) BW_CHECK((bwm_launch<BW_TN, BWE_WGRAD>(g, b.max_rows, st)));
+    else BW_CHECK((bw_launch<BW_TN, BWE_WGRAD, ET, float, float>(g, b.max_rows, st)));
+    return hipSuccess;
+}
+
+template <typename ET>
+static hipError_t layer_backward_t(const BackwardArgs& b, hipStream_t st) {
+    const int64_t T = b.T;
+    const int d = b.d, E = b.E, k = b.k, F = b.dff;
+    // g and da: bf16 operands of the matrix cores in bf16 layers, fp32 otherwise
+    using TG = typename std::conditional<sizeof(ET) == 2, uint16_t, float>::type;
+    // 1. combine backward
+    hipLaunchKernelGGL(combine_backward_kernel<TG>, dim3((unsigned)T), dim3(256), 0, st, T, d, k, b.dy, b.out_perm,
+                       b.slot, b.topk_w, reinterpret_cast<TG*>(b.g), b.dw);
+    BW_CHECK(hipGetLastError());
+    // 2-5. expert FFN
+    BW_CHECK(ffn_backward_t<ET>(b, st));
     // 6. bias gradients
     {
         const int64_t n2 = (int64_t)E * d, n1 = (int64_t)E * F;
-        hipLaunchKernelGGL(segment_colsum_kernel, dim3((unsigned)((n2 + 255) / 256)), dim3(256), 0, st, b.g,
-                           b.offsets, E, (int64_t)0, d, b.db2);
+        hipLaunchKernelGGL(segment_colsum_kernel<TG>, dim3((unsigned)((n2 + 255) / 256)), dim3(256), 0, st,
+                           reinterpret_cast<const TG*>(b.g), b.offsets, E, (int64_t)0, d, b.db2);
         BW_CHECK(hipGetLastError());
-        hipLaunchKernelGGL(segment_colsum_kernel, dim3((unsigned)((n1 + 255) / 256)), dim3(256), 0, st, b.da,
-                           b.offsets, E, (int64_t)0, F, b.db1);
+        hipLaunchKernelGGL(segment_colsum_kernel<TG>, dim3((unsigned)((n1 + 255) / 256)), dim3(256), 0, st,
+                           reinterpret_cast<const TG*>(b.da), b.offsets, E, (int64_t)0, F, b.db1);
         BW_CHECK(hipGetLastError());
     }
-    // 7. gate
+    // 7. gate (fp32 vector ALUs)
     hipLaunchKernelGGL(gate_backward_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, st, T, E, k, b.tau,
                        b.topk_idx, b.topk_w, b.dw, b.dl);
     BW_CHECK(hipGetLastError());
-    g = BwGemmArgs{};
+    BwGemmArgs g{};
     g.A = b.x; g.lda = d;
     g.B = b.dl; g.ldb = E;
     g.E = 1; g.M = d; g.N = E; g.K = (int)T;
     g.C = b.dWg;
     BW_CHECK((bw_launch<BW_TN, BWE_WGRAD, ET, float, float>(g, b.max_rows, st)));
-    hipLaunchKernelGGL(segment_colsum_kernel, dim3((unsigned)((E + 255) / 256)), dim3(256), 0, st, b.dl,
+    hipLaunchKernelGGL(segment_colsum_kernel<float>, dim3((unsigned)((E + 255) / 256)), dim3(256), 0, st, b.dl,
                        (const int32_t*)nullptr, 1, T, E, b.dbg);
     BW_CHECK(hipGetLastError());
     g = BwGemmArgs{};
