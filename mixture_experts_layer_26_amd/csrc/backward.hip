@@ -89,8 +89,16 @@ __global__ __launch_bounds__(BW_THREADS) void bw_gemm_kernel(BwGemmArgs g) {
         m0 = (rest / ntn) * BW_BM;
         n0 = (rest % ntn) * BW_BN;
         mrows = min(BW_BM, g.M - m0);
-        kb = g.offsets ? g.offsets[e] : 0;
-        kend = g.offsets ? g.offsets[e + 1] : g.K;
+        if (g.offsets) {
+            kb = g.offsets[e];
+            kend = g.offsets[e + 1];
+        } else if (g.chunk > 0) {   // split K: output e is the partial sum over chunk e
+            kb = e * g.chunk;
+            kend = min(g.K, kb + g.chunk);
+        } else {
+            kb = 0;
+            kend = g.K;
+        }
     } else {
         int total_mt;
         if (g.offsets) {
@@ -213,14 +221,16 @@ __global__ __launch_bounds__(BW_THREADS) void bw_gemm_kernel(BwGemmArgs g) {
 }
 
 // bf16 layers: the same three patterns on v_mfma_f32_16x16x32_bf16, 128 x
-// 128 outputs per workgroup (four waves of 64 x 64), K in steps of 32.  Both
-// LDS tiles hold their operand K-contiguous ([row][k], rows padded to 40
-// elements so the 16 rows a fragment read touches fall on disjoint banks);
-// a K-contiguous global operand is staged with 16-byte loads and stores, an
-// M/N-contiguous one (the weight W1 of the recompute, both operands of the
-// weight gradients) with 16-byte loads and 2-byte transposing stores.  The
+// 128 outputs per workgroup (four waves of 64 x 64), K in steps of 32.  An
+// operand keeps its global layout in LDS, staged with 16-byte loads and
+// stores: K-contiguous ones as [row][k] (rows padded to 40 elements so the
+// 16 rows of a fragment read fall on disjoint banks), read with
+// ds_read_b128; M/N-contiguous ones (W1 in the recompute, both operands of
+// the weight gradients) as [k][row] (padded to 136), read with
+// ds_read_b64_tr_b16, which hands each lane the K-run of its own row.  The
 // next K-step's global loads are in flight during the current MFMAs.
-constexpr int BWM_BM = 128, BWM_BN = 128, BWM_BK = 32, BWM_LDK = BWM_BK + 8;
+constexpr int BWM_BM = 128, BWM_BN = 128, BWM_BK = 32, BWM_LDK = BWM_BK + 8, BWM_LDM = BWM_BM + 8;
+constexpr int BWM_TILE = BWM_BM * BWM_LDK > BWM_BK * BWM_LDM ? BWM_BM * BWM_LDK : BWM_BK * BWM_LDM;
 
 template <bool KC>   // KC: the operand is K-contiguous in global memory
 __device__ __forceinline__ void bwm_load(const uint16_t* p, int64_t ld, int r0, int rlim, int k0, int kend, int tid,
@@ -251,20 +261,32 @@ __device__ __forceinline__ void bwm_store(uint16_t* s, int tid, const uint4 (&re
             *reinterpret_cast<uint4*>(s + r * BWM_LDK + kc) = reg[q];
         } else {
             const int k = c >> 4, rc = (c & 15) * 8;
-            const uint32_t w[4] = {reg[q].x, reg[q].y, reg[q].z, reg[q].w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                s[(rc + 2 * i) * BWM_LDK + k] = (uint16_t)(w[i] & 0xffffu);
-                s[(rc + 2 * i + 1) * BWM_LDK + k] = (uint16_t)(w[i] >> 16);
-            }
+            *reinterpret_cast<uint4*>(s + k * BWM_LDM + rc) = reg[q];
         }
+    }
+}
+
+// fragment of rows base..base+15 (lane l: row base + l % 16, K 8 (l / 16)..+7)
+template <bool KC>
+__device__ __forceinline__ bf16x8_t bwm_frag(const uint16_t* s, int base, int lane) {
+    const int g16 = lane >> 4, i16 = lane & 15;
+    if constexpr (KC) {
+        return *reinterpret_cast<const bf16x8_t*>(&s[(base + i16) * BWM_LDK + 8 * g16]);
+    } else {
+        // each 16-lane group reads K rows 8 g16 + (i16 >> 2) (+4) at columns
+        // base + 4 (i16 & 3)..+3; the transposing read returns row base + i16
+        const int k = 8 * g16 + (i16 >> 2), col = base + 4 * (i16 & 3);
+        const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MOE_LDS bf16x4_t*)(&s[k * BWM_LDM + col]));
+        const bf16x4_t hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MOE_LDS bf16x4_t*)(&s[(k + 4) * BWM_LDM + col]));
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
 }
 
 template <int MODE, int EPI>
 __global__ __launch_bounds__(256) void bw_mfma_kernel(BwGemmArgs g) {
-    __shared__ __attribute__((aligned(16))) uint16_t As[BWM_BM * BWM_LDK];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[BWM_BN * BWM_LDK];
+    __shared__ __attribute__((aligned(16))) uint16_t As[BWM_TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[BWM_TILE];
     __shared__ int mt_pre[1025];
     __shared__ int scan_tmp[32];
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
@@ -324,8 +346,8 @@ __global__ __launch_bounds__(256) void bw_mfma_kernel(BwGemmArgs g) {
         bf16x8_t af[4], bfr[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            af[i] = *reinterpret_cast<const bf16x8_t*>(&As[(wm * 64 + i * 16 + (lane & 15)) * BWM_LDK + 8 * (lane >> 4)]);
-            bfr[i] = *reinterpret_cast<const bf16x8_t*>(&Bs[(wn * 64 + i * 16 + (lane & 15)) * BWM_LDK + 8 * (lane >> 4)]);
+            af[i] = bwm_frag<AKC>(As, wm * 64 + i * 16, lane);
+            bfr[i] = bwm_frag<BKC>(Bs, wn * 64 + i * 16, lane);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -418,6 +440,33 @@ __global__ __launch_bounds__(256) void segment_colsum_kernel(const TS* __restric
     const int r0 = offsets ? offsets[e] : 0, r1 = offsets ? offsets[e + 1] : (int)rows;
     float s = 0.0f;
     for (int r = r0; r < r1; ++r) s += ld_elem<TS>(src, (int64_t)r * N + c);
+    out[i] = s;
+}
+
+// column sums of a [rows][N] fp32 matrix, one workgroup per column: fixed
+// per-thread row sets and a fixed reduction tree (bitwise repeatable)
+__global__ __launch_bounds__(256) void colsum_long_kernel(const float* __restrict__ src, int64_t rows, int N,
+                                                          float* __restrict__ out) {
+    __shared__ float part[256];
+    const int c = blockIdx.x;
+    float s = 0.0f;
+    for (int64_t r = threadIdx.x; r < rows; r += 256) s += src[r * N + c];
+    part[threadIdx.x] = s;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if (threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) out[c] = part[0];
+}
+
+// out[i] = sum over p of part[p][i], p in order
+__global__ __launch_bounds__(256) void sum_partials_kernel(const float* __restrict__ part, int np, int64_t n,
+                                                           float* __restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    float s = 0.0f;
+    for (int p = 0; p < np; ++p) s += part[(int64_t)p * n + i];
     out[i] = s;
 }
 
@@ -559,14 +608,20 @@ static hipError_t layer_backward_t(const BackwardArgs& b, hipStream_t st) {
     hipLaunchKernelGGL(gate_backward_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, st, T, E, k, b.tau,
                        b.topk_idx, b.topk_w, b.dw, b.dl);
     BW_CHECK(hipGetLastError());
+    // dWg = x^T dl, split over token chunks (partials summed in chunk order)
     BwGemmArgs g{};
     g.A = b.x; g.lda = d;
     g.B = b.dl; g.ldb = E;
-    g.E = 1; g.M = d; g.N = E; g.K = (int)T;
-    g.C = b.dWg;
+    g.E = b.gate_chunks; g.chunk = b.gate_chunk; g.M = d; g.N = E; g.K = (int)T;
+    g.C = b.dwg_part;
     BW_CHECK((bw_launch<BW_TN, BWE_WGRAD, ET, float, float>(g, b.max_rows, st)));
-    hipLaunchKernelGGL(segment_colsum_kernel<float>, dim3((unsigned)((E + 255) / 256)), dim3(256), 0, st, b.dl,
-                       (const int32_t*)nullptr, 1, T, E, b.dbg);
+    {
+        const int64_t n = (int64_t)d * E;
+        hipLaunchKernelGGL(sum_partials_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, b.dwg_part,
+                           b.gate_chunks, n, b.dWg);
+        BW_CHECK(hipGetLastError());
+    }
+    hipLaunchKernelGGL(colsum_long_kernel, dim3((unsigned)E), dim3(256), 0, st, b.dl, T, E, b.dbg);
     BW_CHECK(hipGetLastError());
     g = BwGemmArgs{};
     g.A = b.dl; g.lda = E;

@@ -6,6 +6,7 @@
 // happens on the hot path.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -430,7 +431,8 @@ int moe_aux_loss_ex(const moe_shape* s, int mode, const int32_t* load, float* au
 }
 
 struct BwLayout {
-    size_t g, h, hgrad, da, dx_perm, dw, dl, dxg, total;
+    size_t g, h, hgrad, da, dx_perm, dw, dl, dxg, dwg_part, total;
+    int gate_chunks, gate_chunk;
 };
 
 static BwLayout bw_layout(const Geo& g) {
@@ -450,6 +452,10 @@ static BwLayout bw_layout(const Geo& g) {
     L.dw = take(4 * (size_t)(g.T * g.k));
     L.dl = take(4 * (size_t)(g.T * g.E));
     L.dxg = take(4 * (size_t)(g.T * g.d));
+    // dWg over token chunks of at least 512 rows, at most 64 chunks
+    L.gate_chunks = (int)std::min<int64_t>(64, (g.T + 511) / 512);
+    L.gate_chunk = (int)((g.T + L.gate_chunks - 1) / L.gate_chunks);
+    L.dwg_part = take(4 * (size_t)L.gate_chunks * g.d * g.E);
     L.total = p;
     return L;
 }
@@ -510,6 +516,9 @@ int moe_layer_backward(const moe_shape* s, const void* x, const float* Wg, const
     b.dw = at<float>(ws, L.dw);
     b.dl = at<float>(ws, L.dl);
     b.dxg = at<float>(ws, L.dxg);
+    b.dwg_part = at<float>(ws, L.dwg_part);
+    b.gate_chunks = L.gate_chunks;
+    b.gate_chunk = L.gate_chunk;
     hipStream_t st = static_cast<hipStream_t>(stream);
     MOE_HIP(launch_layer_backward(b, s->dtype, st), "backward kernel launch");
     return MOE_OK;

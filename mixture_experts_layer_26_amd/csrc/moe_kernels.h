@@ -98,8 +98,9 @@ struct BwGemmArgs {
     const void* B;
     int64_t lda, ldb;
     int64_t b_estride;       // elements between experts' weight matrices (NN, NT)
-    const int32_t* offsets;  // row segments [E+1], or null: one segment
+    const int32_t* offsets;  // row segments [E+1], or null: one segment (TN: E chunks of `chunk` rows)
     int E, M, N, K;
+    int chunk;               // TN without offsets: rows per chunk (0: all K rows in one)
     const float* bias;       // NN recompute: b1 [E, N]
     void* C;                 // output
     float* C2;               // NN: GELU'(a) out; NT with GELU' product: GELU'(a) in
@@ -121,6 +122,8 @@ struct BackwardArgs {
     float* dw;       // [T, k]
     float* dl;       // [T, E]
     float* dxg;      // [T, d]
+    float* dwg_part; // [gate_chunks, d, E] partial dWg over token chunks
+    int gate_chunks, gate_chunk;
 };
 hipError_t launch_layer_backward(const BackwardArgs& b, int dtype, hipStream_t st);
 
