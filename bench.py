@@ -266,7 +266,9 @@ def time_router_variant(moe, s, cfg, d, ws, stream):
     us_loss = _median_us(lambda: moe.moe_aux_loss_ex(s1, moe.MOE_LOSS_VARIANCE, routed, aux, stream=stream), stream)
     state = moe.window_state(E, 100, dev)
     pbar = torch.empty(E, dtype=torch.float32, device=dev)
-    us_window = _median_us(lambda: moe.moe_aux_loss_window(s1, routed, state, 100, aux, pbar, stream=stream), stream)
+    aux_w = torch.empty(1, dtype=torch.float32, device=dev)
+    us_window = _median_us(lambda: moe.moe_aux_loss_window(s1, routed, state, 100, aux_w, pbar, stream=stream),
+                           stream)
     nbytes = 3 * T * E * 4 + 8 * T
     return {"top1_noisy_us": us_route, "top1_noisy_bytes": nbytes, "window_loss_us": us_window,
             "top1_noisy_GB/s": nbytes / (us_route * 1e-6) / 1e9,
