@@ -430,7 +430,7 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(int64_t T, int d,
 }
 
 // column sums over row segments: out[e][c] = sum_{r in segment e} src[r][c]
-// (fp32, rows in order); one thread per (expert, column)
+// (fp32, rows in order); one thread per (expert, column) -- fp32 layers
 template <typename TS>
 __global__ __launch_bounds__(256) void segment_colsum_kernel(const TS* __restrict__ src, const int32_t* offsets,
                                                              int E, int64_t rows, int N, float* __restrict__ out) {
@@ -441,6 +441,40 @@ __global__ __launch_bounds__(256) void segment_colsum_kernel(const TS* __restric
     float s = 0.0f;
     for (int r = r0; r < r1; ++r) s += ld_elem<TS>(src, (int64_t)r * N + c);
     out[i] = s;
+}
+
+// column sums over the row segments of a bf16 [rows][N] matrix (N a
+// multiple of 8): a workgroup takes one expert and 512 columns; its 256
+// threads are 4 row groups x 64 column lanes of 8 columns (16-byte loads),
+// the row groups walk rows g, g+4, ... and are added in a fixed order
+// (bitwise repeatable)
+__global__ __launch_bounds__(256) void segment_colsum_bf16_kernel(const uint16_t* __restrict__ src,
+                                                                  const int32_t* __restrict__ offsets, int N,
+                                                                  float* __restrict__ out) {
+    __shared__ float part[4][512];
+    const int e = blockIdx.y;
+    const int grp = threadIdx.x >> 6, cl = threadIdx.x & 63;
+    const int c0 = blockIdx.x * 512 + cl * 8;
+    const int r0 = offsets[e], r1 = offsets[e + 1];
+    float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (c0 < N) {
+        for (int r = r0 + grp; r < r1; r += 4) {
+            const uint4 v = *reinterpret_cast<const uint4*>(src + (int64_t)r * N + c0);
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                s[2 * i] += __uint_as_float(w[i] << 16);
+                s[2 * i + 1] += __uint_as_float(w[i] & 0xffff0000u);
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) part[grp][cl * 8 + i] = s[i];
+    __syncthreads();
+    for (int c = threadIdx.x; c < 512; c += 256) {
+        const int col = blockIdx.x * 512 + c;
+        if (col < N) out[(int64_t)e * N + col] = ((part[0][c] + part[1][c]) + part[2][c]) + part[3][c];
+    }
 }
 
 // column sums of a [rows][N] fp32 matrix, one workgroup per column: fixed
@@ -595,7 +629,14 @@ static hipError_t layer_backward_t(const BackwardArgs& b, hipStream_t st) {
     // 2-5. expert FFN
     BW_CHECK(ffn_backward_t<ET>(b, st));
     // 6. bias gradients
-    {
+    if constexpr (sizeof(ET) == 2) {
+        hipLaunchKernelGGL(segment_colsum_bf16_kernel, dim3((unsigned)((d + 511) / 512), (unsigned)E), dim3(256), 0,
+                           st, reinterpret_cast<const uint16_t*>(b.g), b.offsets, d, b.db2);
+        BW_CHECK(hipGetLastError());
+        hipLaunchKernelGGL(segment_colsum_bf16_kernel, dim3((unsigned)((F + 511) / 512), (unsigned)E), dim3(256), 0,
+                           st, reinterpret_cast<const uint16_t*>(b.da), b.offsets, F, b.db1);
+        BW_CHECK(hipGetLastError());
+    } else {
         const int64_t n2 = (int64_t)E * d, n1 = (int64_t)E * F;
         hipLaunchKernelGGL(segment_colsum_kernel<TG>, dim3((unsigned)((n2 + 255) / 256)), dim3(256), 0, st,
                            reinterpret_cast<const TG*>(b.g), b.offsets, E, (int64_t)0, d, b.db2);
