@@ -227,8 +227,9 @@ __global__ __launch_bounds__(BW_THREADS) void bw_gemm_kernel(BwGemmArgs g) {
 // 16 rows of a fragment read fall on disjoint banks), read with
 // ds_read_b128; M/N-contiguous ones (W1 in the recompute, both operands of
 // the weight gradients) as [k][row] (padded to 136), read with
-// ds_read_b64_tr_b16, which hands each lane the K-run of its own row.  The
-// next K-step's global loads are in flight during the current MFMAs.
+// ds_read_b64_tr_b16, which hands each lane the K-run of its own row.  Two
+// LDS buffers: a step multiplies one while the next tile goes into the
+// other and the one after is loaded into registers.
 constexpr int BWM_BM = 128, BWM_BN = 128, BWM_BK = 32, BWM_LDK = BWM_BK + 8, BWM_LDM = BWM_BM + 8;
 constexpr int BWM_TILE = BWM_BM * BWM_LDK > BWM_BK * BWM_LDM ? BWM_BM * BWM_LDK : BWM_BK * BWM_LDM;
 
@@ -285,8 +286,8 @@ __device__ __forceinline__ bf16x8_t bwm_frag(const uint16_t* s, int base, int la
 
 template <int MODE, int EPI>
 __global__ __launch_bounds__(256) void bw_mfma_kernel(BwGemmArgs g) {
-    __shared__ __attribute__((aligned(16))) uint16_t As[BWM_TILE];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[BWM_TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][BWM_TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BWM_TILE];
     __shared__ int mt_pre[1025];
     __shared__ int scan_tmp[32];
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
@@ -336,24 +337,37 @@ __global__ __launch_bounds__(256) void bw_mfma_kernel(BwGemmArgs g) {
         if constexpr (BKC) bwm_load<true>(Bb, g.ldb, n0, nrows, k0, kend, tid, rb);
         else bwm_load<false>(Bb, g.ldb, n0, nrows, k0, kend, tid, rb);
     };
-    if (kb < kend) load(kb);
-    for (int k0 = kb; k0 < kend; k0 += BWM_BK) {
-        __syncthreads();   // the previous step's fragment reads are done
-        bwm_store<AKC>(As, tid, ra);
-        bwm_store<BKC>(Bs, tid, rb);
+    // two LDS buffers: step s multiplies buffer s & 1 while the tile of step
+    // s + 1 (loaded into registers during step s - 1) is stored into the
+    // other one and the tile of step s + 2 is loaded; one barrier per step
+    if (kb < kend) {
+        load(kb);
+        bwm_store<AKC>(As[0], tid, ra);
+        bwm_store<BKC>(Bs[0], tid, rb);
+        if (kb + BWM_BK < kend) load(kb + BWM_BK);
         __syncthreads();
-        if (k0 + BWM_BK < kend) load(k0 + BWM_BK);
+    }
+    int buf = 0;
+    for (int k0 = kb; k0 < kend; k0 += BWM_BK) {
         bf16x8_t af[4], bfr[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            af[i] = bwm_frag<AKC>(As, wm * 64 + i * 16, lane);
-            bfr[i] = bwm_frag<BKC>(Bs, wn * 64 + i * 16, lane);
+            af[i] = bwm_frag<AKC>(As[buf], wm * 64 + i * 16, lane);
+            bfr[i] = bwm_frag<BKC>(Bs[buf], wn * 64 + i * 16, lane);
+        }
+        if (k0 + BWM_BK < kend) {
+            // the other buffer was last read in step s - 1, before the barrier
+            bwm_store<AKC>(As[buf ^ 1], tid, ra);
+            bwm_store<BKC>(Bs[buf ^ 1], tid, rb);
+            if (k0 + 2 * BWM_BK < kend) load(k0 + 2 * BWM_BK);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+        __syncthreads();
+        buf ^= 1;
     }
 
     // lane l of block [i][j]: row 16 i + l % 16, columns 16 j + 4 (l / 16)..+3
