@@ -594,38 +594,80 @@ static hipError_t ffn_backward_t(const BackwardArgs& b, hipStream_t st) {
     g.B = b.W1; g.ldb = F; g.b_estride = (int64_t)d * F;
     g.offsets = b.offsets; g.E = E; g.K = d; g.N = F;
     g.bias = b.b1; g.C = b.h; g.C2 = b.hgrad;
-    if constexpr (kMfma) BW_CHECK((bwm_launch<BW_NN, BWE_HGRAD>(g, b.max_rows, st)));
-    else BW_CHECK((bw_launch<BW_NN, BWE_HGRAD, ET, ET, ET>(g, b.max_rows, st)));
+    if constexpr (kMfma) {
+        // large problems: the forward's pipelined GEMM with a GELU + GELU' epilogue
+        GemmArgs p{};
+        p.A = b.x_perm; p.B = b.W1; p.bias = b.b1; p.offsets = b.offsets;
+        p.E = E; p.K = d; p.N = F; p.out = b.h; p.out2 = b.hgrad;
+        hipError_t err = hipSuccess;
+        if (launch_ffn_gemm_bf16_pipe(p, EPI_HGRAD, false, b.max_rows, st, &err)) BW_CHECK(err);
+        else BW_CHECK((bwm_launch<BW_NN, BWE_HGRAD>(g, b.max_rows, st)));
+    } else {
+        BW_CHECK((bw_launch<BW_NN, BWE_HGRAD, ET, ET, ET>(g, b.max_rows, st)));
+    }
     // 3. dh = g W2[e]^T (W2[e] stored [F][d] = [N][K]), da = dh * GELU'(a)
     g = BwGemmArgs{};
     g.A = b.g; g.lda = d;
     g.B = b.W2; g.ldb = d; g.b_estride = (int64_t)F * d;
     g.offsets = b.offsets; g.E = E; g.K = d; g.N = F;
     g.C = b.da; g.C2 = b.hgrad;
-    if constexpr (kMfma) BW_CHECK((bwm_launch<BW_NT, BWE_DA>(g, b.max_rows, st)));
-    else BW_CHECK((bw_launch<BW_NT, BWE_DA, float, ET, float>(g, b.max_rows, st)));
+    if constexpr (kMfma) {
+        // large problems: the pipelined GEMM, W2[e] read K-contiguous, GELU' product epilogue
+        GemmArgs p{};
+        p.A = b.g; p.B = b.W2; p.bias = nullptr; p.offsets = b.offsets;
+        p.E = E; p.K = d; p.N = F; p.out = b.da; p.out2 = b.hgrad;
+        hipError_t err = hipSuccess;
+        if (launch_ffn_gemm_bf16_pipe(p, EPI_DA, true, b.max_rows, st, &err)) BW_CHECK(err);
+        else BW_CHECK((bwm_launch<BW_NT, BWE_DA>(g, b.max_rows, st)));
+    } else {
+        BW_CHECK((bw_launch<BW_NT, BWE_DA, float, ET, float>(g, b.max_rows, st)));
+    }
     // 4. dx_perm = da W1[e]^T (W1[e] stored [d][F] = [N][K])
     g = BwGemmArgs{};
     g.A = b.da; g.lda = F;
     g.B = b.W1; g.ldb = F; g.b_estride = (int64_t)d * F;
     g.offsets = b.offsets; g.E = E; g.K = F; g.N = d;
     g.C = b.dx_perm;
-    if constexpr (kMfma) BW_CHECK((bwm_launch<BW_NT, BWE_STORE>(g, b.max_rows, st)));
-    else BW_CHECK((bw_launch<BW_NT, BWE_STORE, float, ET, float>(g, b.max_rows, st)));
+    if constexpr (kMfma) {
+        // large problems: the pipelined GEMM with W1[e] read K-contiguous
+        GemmArgs p{};
+        p.A = b.da; p.B = b.W1; p.bias = nullptr; p.offsets = b.offsets;
+        p.E = E; p.K = F; p.N = d; p.out = b.dx_perm;
+        hipError_t err = hipSuccess;
+        if (launch_ffn_gemm_bf16_pipe(p, EPI_STORE_F32, true, b.max_rows, st, &err)) BW_CHECK(err);
+        else BW_CHECK((bwm_launch<BW_NT, BWE_STORE>(g, b.max_rows, st)));
+    } else {
+        BW_CHECK((bw_launch<BW_NT, BWE_STORE, float, ET, float>(g, b.max_rows, st)));
+    }
     // 5. dW2[e] = h^T g  ([F][d]), dW1[e] = x_perm^T da  ([d][F])
     g = BwGemmArgs{};
     g.A = b.h; g.lda = F;
     g.B = b.g; g.ldb = d;
     g.offsets = b.offsets; g.E = E; g.M = F; g.N = d;
     g.C = b.dW2;
-    if constexpr (kMfma) BW_CHECK((bwm_launch<BW_TN, BWE_WGRAD>(g, b.max_rows, st)));
+    // long row segments (>= 1024 rows per expert on average, bounded by
+    // max_rows): the pipelined GEMM in its weight-gradient form.  Short ones
+    // keep the 128 x 128 kernel: there every 256 x 256 item is a few K-steps
+    // followed by 256 KiB of fp32 stores, and the next item's waits (vmcnt
+    // counts stores and loads in one order) hold its loads behind them.
+    auto wgrad = [&](const BwGemmArgs& w) -> hipError_t {
+        if (b.max_rows >= 1024LL * E) {
+            GemmArgs p{};
+            p.A = w.A; p.B = w.B; p.bias = nullptr; p.offsets = w.offsets;
+            p.E = w.E; p.M = w.M; p.N = w.N; p.out = w.C;
+            hipError_t err = hipSuccess;
+            if (launch_ffn_gemm_bf16_pipe(p, EPI_WGRAD, false, b.max_rows, st, &err)) return err;
+        }
+        return bwm_launch<BW_TN, BWE_WGRAD>(w, b.max_rows, st);
+    };
+    if constexpr (kMfma) BW_CHECK(wgrad(g));
     else BW_CHECK((bw_launch<BW_TN, BWE_WGRAD, ET, float, float>(g, b.max_rows, st)));
     g = BwGemmArgs{};
     g.A = b.x_perm; g.lda = d;
     g.B = b.da; g.ldb = F;
     g.offsets = b.offsets; g.E = E; g.M = d; g.N = F;
     g.C = b.dW1;
-    if constexpr (kMfma) BW_CHECK((bwm_launch<BW_TN, BWE_WGRAD>(g, b.max_rows, st)));
+    if constexpr (kMfma) BW_CHECK(wgrad(g));
     else BW_CHECK((bw_launch<BW_TN, BWE_WGRAD, ET, float, float>(g, b.max_rows, st)));
     return hipSuccess;
 }

@@ -188,38 +188,67 @@ __device__ __forceinline__ void build_padded_offsets(const int* s_off, int E, in
 template <class C>
 struct Item {
     int e, m0, mrows, n0;
-    int pm0;   // first padded row (h tile layout)
+    int pm0;         // first padded row (h tile layout)
+    int nk, nks;     // K-steps of the item, and rounded up to even
+    int mc0, k0;     // transposed form: first column of A, first segment row
     i32x4_t rsA, rsB;
     int a_off[C::A_DMA], b_off[C::B_DMA];
 };
 
-template <class C, bool AT>   // AT: A in the h tile layout
+// AT: A in the h tile layout; BKC: B stored [E, N, K] (K-contiguous rows of
+// N, staged like the activations) instead of [E, K, N].
+// TN (weight gradients): out[e] [M, N] = A[seg(e)]^T B[seg(e)], both operands
+// [rows, M] / [rows, N] row-major over the expert's segment of rows, so K is
+// the segment and varies per item; A is staged like the weights ([k][m]
+// rows) and read with transposing reads.  Items are (expert, m-tile,
+// n-tile) over every expert; an expert without rows has no K-steps and gets
+// zeros.
+template <class C, bool AT, bool BKC = false, bool TN = false>
 struct Loader {
     const uint16_t* A;
     const uint16_t* Bw;
     const int* s_off;    // expert row offsets, copied to LDS
     const int* mt_pre;   // m-tile prefix, LDS
     const int* s_poff;   // padded expert row offsets (h tile layout), LDS
-    int E, K, N, ntn, wid;
-    int a_rl, a_ps, b_rl, b_pc;
+    int E, K, N, M, ntn, mtn, wid;
+    int a_rl, a_ps, b_rl, b_pc;   // BKC: b_rl, b_pc as a_rl, a_ps
     int a_kt;            // A in the tile layout: 32-column tiles per 16-row block
     static constexpr int B_ROWS_PER_DMA = 512 / C::BN;
 
     __device__ __forceinline__ Loader(const GemmArgs& g, const int* off, const int* pre, const int* poff, int ntn_,
                                       int wid_, int lane)
         : A(static_cast<const uint16_t*>(g.A)), Bw(static_cast<const uint16_t*>(g.B)), s_off(off),
-          mt_pre(pre), s_poff(poff), E(g.E), K(g.K), N(g.N), ntn(ntn_), wid(wid_) {
+          mt_pre(pre), s_poff(poff), E(g.E), K(g.K), N(g.N), M(g.M), ntn(ntn_), wid(wid_) {
         a_kt = (g.K + 31) >> 5;
+        mtn = (g.M + C::BM - 1) / C::BM;
         // A: a wave instruction covers 16 rows; lane -> (row, physical slot)
-        a_rl = lane >> 2;
-        a_ps = lane & 3;
+        // (TN: 512 / BM k-rows; lane -> (k-row, physical chunk))
+        a_rl = TN ? lane / (C::BM / 8) : lane >> 2;
+        a_ps = TN ? lane % (C::BM / 8) : lane & 3;
         // B: a wave instruction covers 512 / BN k-rows; lane -> (k-row, physical chunk)
-        b_rl = lane / C::B_ROW_CHUNKS;
-        b_pc = lane % C::B_ROW_CHUNKS;
+        // (BKC: 16 rows of N, as A)
+        b_rl = BKC ? lane >> 2 : lane / C::B_ROW_CHUNKS;
+        b_pc = BKC ? lane & 3 : lane % C::B_ROW_CHUNKS;
     }
 
     // expert, first row, row count and first column of an item (LDS reads only)
     __device__ __forceinline__ void decode(int64_t item, Item<C>& it) const {
+        if constexpr (TN) {
+            const int per_e = mtn * ntn;
+            const int e = __builtin_amdgcn_readfirstlane((int)(item / per_e));
+            const int rest = __builtin_amdgcn_readfirstlane((int)(item - (int64_t)e * per_e));
+            const int mt = rest / ntn;
+            it.e = e;
+            it.mc0 = mt * C::BM;
+            it.m0 = __builtin_amdgcn_readfirstlane(e * M + it.mc0);   // output row of out [E M, N]
+            it.mrows = __builtin_amdgcn_readfirstlane(min(C::BM, M - it.mc0));
+            it.n0 = __builtin_amdgcn_readfirstlane((rest - mt * ntn) * C::BN);
+            it.pm0 = 0;
+            it.k0 = __builtin_amdgcn_readfirstlane(s_off[e]);
+            it.nk = __builtin_amdgcn_readfirstlane((s_off[e + 1] - it.k0 + BK - 1) / BK);
+            it.nks = it.nk + (it.nk & 1);
+            return;
+        }
         const WorkItem wi = decode_item(mt_pre, E, ntn, item);
         const int e = __builtin_amdgcn_readfirstlane(wi.e);
         const int m0 = __builtin_amdgcn_readfirstlane(s_off[e] + wi.mt * C::BM);
@@ -228,6 +257,8 @@ struct Loader {
         it.mrows = __builtin_amdgcn_readfirstlane(min(C::BM, s_off[e + 1] - m0));
         it.n0 = __builtin_amdgcn_readfirstlane(wi.nt * C::BN);
         it.pm0 = __builtin_amdgcn_readfirstlane(s_poff[e] + wi.mt * C::BM);
+        it.nk = (K + BK - 1) / BK;
+        it.nks = it.nk + (it.nk & 1);
     }
 
     __device__ __forceinline__ void setup(int64_t item, Item<C>& it) const {
@@ -235,7 +266,19 @@ struct Loader {
         // activations: the range ends at the expert's last row, so rows past the
         // segment read zeros; a K tail reads the next row's head, which meets the
         // zero weight rows past K (finite inputs)
-        if constexpr (AT) {
+        if constexpr (TN) {
+            // both operands: the expert's rows; rows past the segment read zeros
+            const uint32_t rows = (uint32_t)(s_off[it.e + 1] - it.k0);
+            it.rsA = make_rsrc(A + (int64_t)it.k0 * M, rows * (uint32_t)M * 2u);
+            it.rsB = make_rsrc(Bw + (int64_t)it.k0 * N, rows * (uint32_t)N * 2u);
+#pragma unroll
+            for (int j = 0; j < C::A_DMA; ++j) {
+                const int k = (wid * C::A_DMA + j) * (512 / C::BM) + a_rl;   // tile k-row
+                const int c = a_ps ^ b_swz<C::MF>(k);                          // logical chunk
+                const int col = it.mc0 + c * 8;
+                it.a_off[j] = (col < M) ? (k * M + col) * 2 : kOutOfRange;
+            }
+        } else if constexpr (AT) {
             // the item's 16-row blocks; rows past the segment inside its last
             // block are padding, later blocks read zeros
             it.rsA = make_rsrc(A + (int64_t)(it.pm0 >> 4) * a_kt * 512,
@@ -243,41 +286,51 @@ struct Loader {
         } else {
             it.rsA = make_rsrc(A + (int64_t)it.m0 * K, (uint32_t)it.mrows * (uint32_t)K * 2u);
         }
-        it.rsB = make_rsrc(Bw + (int64_t)it.e * K * N, (uint32_t)K * (uint32_t)N * 2u);
+        if constexpr (!TN) it.rsB = make_rsrc(Bw + (int64_t)it.e * K * N, (uint32_t)K * (uint32_t)N * 2u);
 #pragma unroll
         for (int j = 0; j < C::A_DMA; ++j) {
+            if constexpr (TN) break;
             const int r = (wid * C::A_DMA + j) * 16 + a_rl;   // tile row
             const int c = a_ps ^ a_swz<C::MF>(r);               // logical chunk
             it.a_off[j] = AT ? ((r >> 4) * a_kt * 512 + (r & 15) * 32 + c * 8) * 2 : (r * K + c * 8) * 2;
         }
 #pragma unroll
         for (int j = 0; j < C::B_DMA; ++j) {
-            const int k = (wid * C::B_DMA + j) * B_ROWS_PER_DMA + b_rl;   // tile k-row
-            const int c = b_pc ^ b_swz<C::MF>(k);                           // logical chunk
-            const int col = it.n0 + c * 8;
-            it.b_off[j] = (col < N) ? (k * N + col) * 2 : kOutOfRange;
+            if constexpr (BKC) {
+                const int r = (wid * C::B_DMA + j) * 16 + b_rl;   // tile row (column n0 + r of the output)
+                const int c = b_pc ^ a_swz<C::MF>(r);              // logical chunk
+                it.b_off[j] = (it.n0 + r < N) ? ((it.n0 + r) * K + c * 8) * 2 : kOutOfRange;
+            } else {
+                const int k = (wid * C::B_DMA + j) * B_ROWS_PER_DMA + b_rl;   // tile k-row
+                const int c = b_pc ^ b_swz<C::MF>(k);                           // logical chunk
+                const int col = it.n0 + c * 8;
+                it.b_off[j] = (col < N) ? (k * N + col) * 2 : kOutOfRange;
+            }
         }
     }
 
     // PER = A_DMA + B_DMA loads of K-step kt of `it` into one ring slot
     __device__ __forceinline__ void issue(const Item<C>& it, int kt, uint16_t* sa_buf, uint16_t* sb_buf) const {
         const int k0 = kt * BK;
-        const int a_step = AT ? kt * 1024 : k0 * 2;   // bytes to K-step kt
+        const int a_step = TN ? k0 * M * 2 : AT ? kt * 1024 : k0 * 2;   // bytes to K-step kt
 #pragma unroll
-        for (int j = 0; j < C::A_DMA; ++j)
-            dma16(it.rsA, sa_buf + (wid * C::A_DMA + j) * 512, it.a_off[j] + a_step);
+        for (int j = 0; j < C::A_DMA; ++j) {
+            const int off = (TN && it.a_off[j] == kOutOfRange) ? kOutOfRange : it.a_off[j] + a_step;
+            dma16(it.rsA, sa_buf + (wid * C::A_DMA + j) * 512, off);
+        }
 #pragma unroll
         for (int j = 0; j < C::B_DMA; ++j) {
-            const int off = (it.b_off[j] == kOutOfRange) ? kOutOfRange : it.b_off[j] + k0 * N * 2;
+            const int step = BKC ? k0 * 2 : k0 * N * 2;
+            const int off = (it.b_off[j] == kOutOfRange) ? kOutOfRange : it.b_off[j] + step;
             dma16(it.rsB, sb_buf + (wid * C::B_DMA + j) * 512, off);
         }
     }
 
     // the item's BN bias values (fp32, 1 KiB) into LDS: one wave instruction,
-    // columns past N read zeros
+    // columns past N (and every column without a bias) read zeros
     __device__ __forceinline__ void issue_bias(const Item<C>& it, const float* bias, int lane, float* dst) const {
         static_assert(C::BN == 256, "one wave instruction per bias slice");
-        const i32x4_t rs = make_rsrc(bias + (int64_t)it.e * N, (uint32_t)N * 4u);
+        const i32x4_t rs = bias ? make_rsrc(bias + (int64_t)it.e * N, (uint32_t)N * 4u) : make_rsrc(bias, 0u);
         dma16(rs, dst, (it.n0 + 4 * lane) * 4);
     }
 
@@ -365,7 +418,7 @@ struct Frags32 {
     bf16x8_t t[C::MB][2];
 };
 
-template <class C>
+template <class C, bool BKC = false, bool TN = false>
 __device__ __forceinline__ void read_frags32(Frags32<C>& f, const uint16_t* as, const uint16_t* bs, int wm, int wn,
                                              int lane) {
     const int g16 = lane >> 4, i16 = lane & 15;
@@ -373,6 +426,12 @@ __device__ __forceinline__ void read_frags32(Frags32<C>& f, const uint16_t* as, 
     for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
+            if constexpr (BKC) {
+                // K-contiguous weight rows, laid out like the activations
+                const int col = wn * C::TN + nb * 32 + (lane & 31);
+                f.w[nb][h] = *reinterpret_cast<const bf16x8_t*>(&bs[a_slot<32>(col, 2 * h + (lane >> 5)) * 8]);
+                continue;
+            }
             // the 16-lane group g16 covers columns 16 (g16 & 1)..+15 of the block and
             // K rows 16 h + 8 (g16 >> 1)..+7: lane i16 points at row (i16 >> 2) (+4),
             // columns 4 (i16 & 3)..+3 of that 4 x 16 window
@@ -387,6 +446,16 @@ __device__ __forceinline__ void read_frags32(Frags32<C>& f, const uint16_t* as, 
     for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
+            if constexpr (TN) {
+                // [k][m] rows, read like the weights
+                const int col = wm * C::TM + mb * 32 + 16 * (g16 & 1) + 4 * (i16 & 3);
+                const int k = 16 * h + 8 * (g16 >> 1) + (i16 >> 2);
+                const int c = col >> 3, half = (col & 7);
+                const bf16x4_t lo = lds_read_tr(&as[k * C::BM + b_chunk<32>(k, c) * 8 + half]);
+                const bf16x4_t hi = lds_read_tr(&as[(k + 4) * C::BM + b_chunk<32>(k + 4, c) * 8 + half]);
+                f.t[mb][h] = cat8(lo, hi);
+                continue;
+            }
             const int r = wm * C::TM + mb * 32 + (lane & 31);
             f.t[mb][h] = *reinterpret_cast<const bf16x8_t*>(&as[a_slot<32>(r, 2 * h + (lane >> 5)) * 8]);
         }
@@ -440,7 +509,7 @@ __device__ __forceinline__ void epilogue32(const GemmArgs& g, const Item<C>& it,
         const int64_t row = it.m0 + ml, prow = it.pm0 + ml;
 #pragma unroll
         for (int nb = 0; nb < C::NB; ++nb) {
-            if constexpr (EPI == EPI_GELU_H) {
+            if constexpr (EPI == EPI_GELU_H || EPI == EPI_HGRAD || EPI == EPI_DA) {
 #pragma unroll
                 for (int q = 0; q < 4; q += 2) {
                     const int nl = wn * C::TN + nb * 32 + 8 * q + 4 * h;
@@ -450,8 +519,30 @@ __device__ __forceinline__ void epilogue32(const GemmArgs& g, const Item<C>& it,
                     for (int j = 0; j < 2; ++j) {
                         const f32x4_t b = *reinterpret_cast<const f32x4_t*>(&sbias[nl + 8 * j]);
                         const int e = 4 * (q + j);
-                        p[j][0] = pack_bf16x2(gelu_as(acc[mb][nb][e] + b[0]), gelu_as(acc[mb][nb][e + 1] + b[1]));
-                        p[j][1] = pack_bf16x2(gelu_as(acc[mb][nb][e + 2] + b[2]), gelu_as(acc[mb][nb][e + 3] + b[3]));
+                        if constexpr (EPI == EPI_DA) {
+                            // dh * GELU'(a): the factor read from out2 (a global load
+                            // here waits for the loads issued before it, in order)
+                            const int ng = it.n0 + nl + 8 * j;
+                            f32x4_t gv = {0.f, 0.f, 0.f, 0.f};
+                            if (row_ok && ng < g.N) gv = *reinterpret_cast<const f32x4_t*>(g.out2 + row * g.N + ng);
+                            p[j][0] = pack_bf16x2(acc[mb][nb][e] * gv[0], acc[mb][nb][e + 1] * gv[1]);
+                            p[j][1] = pack_bf16x2(acc[mb][nb][e + 2] * gv[2], acc[mb][nb][e + 3] * gv[3]);
+                        } else if constexpr (EPI == EPI_HGRAD) {
+                            // GELU'(a) of this lane's quad straight to out2; h as below
+                            float hv[4], ga[4];
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) gelu_and_grad_as(acc[mb][nb][e + i] + b[i], hv[i], ga[i]);
+                            const f32x4_t gv = {ga[0], ga[1], ga[2], ga[3]};
+                            const int ng = it.n0 + nl + 8 * j;
+                            if (row_ok && ng < g.N)
+                                *reinterpret_cast<f32x4_t*>(g.out2 + row * g.N + ng) = gv;
+                            p[j][0] = pack_bf16x2(hv[0], hv[1]);
+                            p[j][1] = pack_bf16x2(hv[2], hv[3]);
+                        } else {
+                            p[j][0] = pack_bf16x2(gelu_as(acc[mb][nb][e] + b[0]), gelu_as(acc[mb][nb][e + 1] + b[1]));
+                            p[j][1] =
+                                pack_bf16x2(gelu_as(acc[mb][nb][e + 2] + b[2]), gelu_as(acc[mb][nb][e + 3] + b[3]));
+                        }
                     }
                     const auto x = __builtin_amdgcn_permlane32_swap(p[0][0], p[1][0], false, false);
                     const auto y = __builtin_amdgcn_permlane32_swap(p[0][1], p[1][1], false, false);
@@ -470,7 +561,8 @@ __device__ __forceinline__ void epilogue32(const GemmArgs& g, const Item<C>& it,
                     const int nl = wn * C::TN + nb * 32 + 8 * q + 4 * h;
                     const int n = it.n0 + nl;
                     if (!row_ok || n >= g.N) continue;
-                    const f32x4_t b = *reinterpret_cast<const f32x4_t*>(&sbias[nl]);
+                    const f32x4_t b = EPI == EPI_WGRAD ? f32x4_t{0.f, 0.f, 0.f, 0.f}
+                                                       : *reinterpret_cast<const f32x4_t*>(&sbias[nl]);
                     const f32x4_t v = {acc[mb][nb][4 * q], acc[mb][nb][4 * q + 1], acc[mb][nb][4 * q + 2],
                                        acc[mb][nb][4 * q + 3]};
                     store4<EPI>(g, row, prow, n, v + b);
@@ -585,7 +677,10 @@ __global__ __launch_bounds__(C::NT) void ffn_gemm_bf16_kernel(GemmArgs g) {
 // (NS >= 3) never overwrite one still in use.
 //
 // WPE: waves per SIMD the kernel is built for (register budget 512 / WPE).
-template <class C, int NS, int EMAX, int WPE, int EPI>
+// AT: A in the h tile layout; BKC: B stored K-contiguous ([E, N, K]); TN:
+// the weight-gradient form of Loader (K-steps per item vary; items without
+// any K-step skip the ring and store zeros).
+template <class C, int NS, int EMAX, int WPE, int EPI, bool AT, bool BKC, bool TN>
 __global__ __launch_bounds__(C::NT, WPE) void ffn_gemm_bf16_pipe_kernel(GemmArgs g) {
     static_assert(C::MF == 32 && C::BN == 256, "256-column tiles on 32x32x16 MFMAs");
     static_assert(NS >= 3 && NS <= 4, "ring depth");
@@ -600,38 +695,55 @@ __global__ __launch_bounds__(C::NT, WPE) void ffn_gemm_bf16_pipe_kernel(GemmArgs
     const int lane = tid & (kWave - 1);
     const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform: scalar branches
     const int wm = wid / C::WN, wn = wid % C::WN;
-    const int E = g.E, K = g.K, N = g.N;
+    const int E = g.E, N = g.N;
     const int ntn = (N + C::BN - 1) / C::BN;
-    const int nk = (K + BK - 1) / BK;
-    const int nks = nk + (nk & 1);   // steps per item, even
 
     for (int i = tid; i <= E; i += C::NT) s_off[i] = g.offsets[i];
-    const int total_mt = build_mtile_prefix(g.offsets, E, C::BM, mt_pre, scan_tmp);   // ends with a barrier
-    build_padded_offsets(s_off, E, s_poff, scan_tmp);
-    const ItemRange range = xcd_item_range((int64_t)total_mt * ntn);
+    int64_t total;
+    if constexpr (TN) {
+        __syncthreads();
+        total = (int64_t)E * ((g.M + C::BM - 1) / C::BM) * ntn;
+    } else {
+        total = (int64_t)build_mtile_prefix(g.offsets, E, C::BM, mt_pre, scan_tmp) * ntn;   // ends with a barrier
+        build_padded_offsets(s_off, E, s_poff, scan_tmp);
+    }
+    const ItemRange range = xcd_item_range(total);
     if (range.first >= range.end) return;
-    const Loader<C, kATiled<EPI>> ld(g, s_off, mt_pre, s_poff, ntn, wid, lane);
+    const Loader<C, AT, BKC, TN> ld(g, s_off, mt_pre, s_poff, ntn, wid, lane);
     constexpr int PER = C::A_DMA + C::B_DMA;
+    constexpr bool kBias = EPI != EPI_WGRAD;
 
-    // load cursor: item, K-step, ring slot and bias slot of the next stage
+    // load cursor: item, K-step, ring slot and bias slot of the next stage;
+    // it passes over items without K-steps (TN)
     Item<C> lit;
     int64_t l_item = range.first;
     int l_kt = 0, l_slot = 0, l_bslot = 0;
     ld.setup(l_item, lit);
+    if constexpr (TN) {
+        while (lit.nks == 0) {
+            l_item += range.step;
+            if (l_item >= range.end) break;
+            ld.setup(l_item, lit);
+        }
+    }
     auto issue_next = [&]() {
         if (l_item < range.end) {
-            if (l_kt == 0 && wid == 0) ld.issue_bias(lit, g.bias, lane, s_bias[l_bslot]);
-            if (l_kt < nk) ld.issue(lit, l_kt, sa[l_slot], sb[l_slot]);
+            if (kBias && l_kt == 0 && wid == 0) ld.issue_bias(lit, g.bias, lane, s_bias[l_bslot]);
+            if (l_kt < lit.nk) ld.issue(lit, l_kt, sa[l_slot], sb[l_slot]);
             else ld.issue_zero(lit, sa[l_slot], sb[l_slot]);
         } else {
             ld.issue_zero(lit, sa[l_slot], sb[l_slot]);
         }
         if (++l_slot == NS) l_slot = 0;
-        if (++l_kt == nks) {
+        if (++l_kt == lit.nks) {
             l_kt = 0;
             if (++l_bslot == NS) l_bslot = 0;
-            l_item += range.step;
-            if (l_item < range.end) ld.setup(l_item, lit);
+            while (true) {
+                l_item += range.step;
+                if (l_item >= range.end) break;
+                ld.setup(l_item, lit);
+                if (!TN || lit.nks > 0) break;
+            }
         }
     };
     for (int s = 0; s < NS; ++s) issue_next();
@@ -639,9 +751,9 @@ __global__ __launch_bounds__(C::NT, WPE) void ffn_gemm_bf16_pipe_kernel(GemmArgs
 
     // GEMM2 keeps C/D in AGPRs (about 4% faster); GEMM1's GELU epilogue does
     // not fit the remaining 128 VGPRs and stays on the VGPR forms
-    if constexpr (EPI == EPI_STORE_F32) request_agpr_accumulators();
+    if constexpr (EPI == EPI_STORE_F32 || EPI == EPI_WGRAD) request_agpr_accumulators();
     Frags32<C> fa, fb;
-    read_frags32<C>(fa, sa[0], sb[0], wm, wn, lane);
+    read_frags32<C, BKC, TN>(fa, sa[0], sb[0], wm, wn, lane);
     int c_slot = 0, c_bslot = 0;
     int64_t item = range.first;
     f32x16_t acc[C::MB][C::NB];
@@ -654,9 +766,9 @@ __global__ __launch_bounds__(C::NT, WPE) void ffn_gemm_bf16_pipe_kernel(GemmArgs
         // global -> LDS loads, then the second K-half: the loads of eight waves
         // take the TA ~500 cycles per step, and issued right after the barrier
         // they held back the MFMAs
-        read_frags32<C>(nxt, sa[ns], sb[ns], wm, wn, lane);
+        read_frags32<C, BKC, TN>(nxt, sa[ns], sb[ns], wm, wn, lane);
         mfma_half32<C>(acc, cur, 0);
-        interleave_mfma_reads<C::MB * C::NB, 4 * C::NB + 2 * C::MB>();
+        interleave_mfma_reads<C::MB * C::NB, (BKC ? 2 : 4) * C::NB + (TN ? 4 : 2) * C::MB>();
         __builtin_amdgcn_sched_barrier(0);
         issue_next();
         __builtin_amdgcn_sched_barrier(0);
@@ -672,13 +784,14 @@ __global__ __launch_bounds__(C::NT, WPE) void ffn_gemm_bf16_pipe_kernel(GemmArgs
             for (int j = 0; j < C::NB; ++j)
 #pragma unroll
                 for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
-        for (int kt = 0; kt < nks; kt += 2) {
+        for (int kt = 0; kt < cur.nks; kt += 2) {
             step(fa, fb);
             step(fb, fa);
         }
         // the bias slice landed with the item's first stage, several barriers ago
         epilogue32<C, EPI>(g, cur, acc, s_bias[c_bslot], wm, wn, lane);
-        if (++c_bslot == NS) c_bslot = 0;
+        if (!TN || cur.nks > 0)
+            if (++c_bslot == NS) c_bslot = 0;
         item += range.step;
         if (item >= range.end) break;
     }
@@ -704,9 +817,10 @@ static int small_blocks() {
 // Large tiles: 256 x 256 on eight waves (two per SIMD), four 32 KiB stages.
 // (Two workgroups per CU on 128 x 256 tiles measured slower where weight
 // tiles are shared by several m-tiles: each re-reads them from HBM.)
-template <class C, int NS, int EMAX, int WPE, int EPI>
+template <class C, int NS, int EMAX, int WPE, int EPI, bool AT, bool BKC, bool TN>
 static int pipe_blocks() {
-    static const int blocks = persistent_blocks(ffn_gemm_bf16_pipe_kernel<C, NS, EMAX, WPE, EPI>, C::NT);
+    static const int blocks =
+        persistent_blocks(ffn_gemm_bf16_pipe_kernel<C, NS, EMAX, WPE, EPI, AT, BKC, TN>, C::NT);
     return blocks;
 }
 
@@ -717,12 +831,15 @@ static int64_t item_bound(const GemmArgs& g, int64_t max_rows) {
     return ((max_rows + C::BM - 1) / C::BM + g.E) * ((g.N + C::BN - 1) / C::BN);
 }
 
-template <class C, int NS, int EMAX, int WPE, int EPI>
+template <class C, int NS, int EMAX, int WPE, int EPI, bool AT = kATiled<EPI>, bool BKC = false, bool TN = false>
 static bool try_pipe(const GemmArgs& g, int64_t max_rows, hipStream_t st, hipError_t* err) {
-    const int blocks = pipe_blocks<C, NS, EMAX, WPE, EPI>();
+    const int blocks = pipe_blocks<C, NS, EMAX, WPE, EPI, AT, BKC, TN>();
     // large tiles need about 3 items per workgroup to keep the tail short
-    if (g.E > EMAX || item_bound<C>(g, max_rows) < 3 * (int64_t)blocks) return false;
-    hipLaunchKernelGGL((ffn_gemm_bf16_pipe_kernel<C, NS, EMAX, WPE, EPI>), dim3(blocks), dim3(C::NT), 0, st, g);
+    const int64_t items = TN ? (int64_t)g.E * ((g.M + C::BM - 1) / C::BM) * ((g.N + C::BN - 1) / C::BN)
+                             : item_bound<C>(g, max_rows);
+    if (g.E > EMAX || items < 3 * (int64_t)blocks) return false;
+    hipLaunchKernelGGL((ffn_gemm_bf16_pipe_kernel<C, NS, EMAX, WPE, EPI, AT, BKC, TN>), dim3(blocks), dim3(C::NT), 0,
+                       st, g);
     *err = hipGetLastError();
     return true;
 }
@@ -738,6 +855,19 @@ static hipError_t launch_epi(const GemmArgs& g, int64_t max_rows, hipStream_t st
 
 hipError_t launch_ffn_gemm_bf16(const GemmArgs& g, int epi, int64_t max_rows, hipStream_t st) {
     return epi == EPI_GELU_H ? launch_epi<EPI_GELU_H>(g, max_rows, st) : launch_epi<EPI_STORE_F32>(g, max_rows, st);
+}
+
+bool launch_ffn_gemm_bf16_pipe(const GemmArgs& g, int epi, bool b_kc, int64_t max_rows, hipStream_t st,
+                               hipError_t* err) {
+    constexpr int WPE = TilePipe::NW >= 8 ? 2 : 1;
+    if (b_kc && g.K % BK != 0) return false;   // both operands K-contiguous: no zero rows under a K tail
+    if (epi == EPI_HGRAD && !b_kc) return try_pipe<TilePipe, 4, 1024, WPE, EPI_HGRAD, false, false>(g, max_rows, st, err);
+    if (epi == EPI_STORE_F32 && b_kc)
+        return try_pipe<TilePipe, 4, 1024, WPE, EPI_STORE_F32, false, true>(g, max_rows, st, err);
+    if (epi == EPI_DA && b_kc) return try_pipe<TilePipe, 4, 1024, WPE, EPI_DA, false, true>(g, max_rows, st, err);
+    if (epi == EPI_WGRAD && !b_kc)
+        return try_pipe<TilePipe, 4, 1024, WPE, EPI_WGRAD, false, false, true>(g, max_rows, st, err);
+    return false;
 }
 
 }  // namespace moe

@@ -60,6 +60,22 @@ __device__ __forceinline__ float gelu_as(float u) {
     return fmaxf(u, 0.0f) - fminf(fabsf(u), 3.40282347e38f) * q;
 }
 
+// GELU and its derivative from one evaluation of the erf approximation of
+// gelu_as: with q = Phi(-|u|), Phi(u) = 1 - q for u >= 0 and q for u < 0, and
+// GELU'(u) = Phi(u) + u phi(u) with phi(u) = exp(-u^2 / 2) / sqrt(2 pi).
+// u must be finite.
+__device__ __forceinline__ void gelu_and_grad_as(float u, float& h, float& hg) {
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f * 0.70710678118654752440f, fabsf(u), 1.0f));
+    float poly = fmaf(t, 0.5f * 1.061405429f, 0.5f * -1.453152027f);
+    poly = fmaf(t, poly, 0.5f * 1.421413741f);
+    poly = fmaf(t, poly, 0.5f * -0.284496736f);
+    poly = fmaf(t, poly, 0.5f * 0.254829592f);
+    const float e = __builtin_amdgcn_exp2f(u * (u * (-0.5f * 1.44269504088896340736f)));
+    const float q = poly * t * e;
+    h = fmaxf(u, 0.0f) - fabsf(u) * q;
+    hg = (u >= 0.0f ? 1.0f - q : q) + u * (e * 0.39894228040143267794f);
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
 #pragma unroll

@@ -58,21 +58,34 @@ hipError_t launch_scatter(const DispatchArgs& a, hipStream_t st);
 hipError_t launch_gather(const DispatchArgs& a, hipStream_t st);
 
 // ---- ffn_bf16.hip / ffn_fp32.hip ----------------------------------------
-enum { EPI_GELU_H = 0, EPI_STORE_F32 = 1 };
+// bf16 pipelined kernel only, for the backward (no bias, [rows, N] row-major):
+//   EPI_HGRAD: h = GELU(a) in bf16 to out and GELU'(a) in fp32 to out2;
+//   EPI_DA: (A B) * out2 (GELU'(a), read) in bf16 to out;
+//   EPI_WGRAD: out[e] [M, N] fp32 = A[seg(e)]^T B[seg(e)] with A [rows, M] and
+//   B [rows, N] row-major (the segments of offsets), zeros for idle experts
+enum { EPI_GELU_H = 0, EPI_STORE_F32 = 1, EPI_HGRAD = 2, EPI_DA = 3, EPI_WGRAD = 4 };
 struct GemmArgs {
     const void* A;           // [rows, K], row-major, layer dtype
-    const void* B;           // [E, K, N], row-major, layer dtype
-    const float* bias;       // [E, N]
+    const void* B;           // [E, K, N], row-major, layer dtype ([E, N, K] for the K-contiguous form)
+    const float* bias;       // [E, N], or null for none (bf16 pipelined kernel)
     const int32_t* offsets;  // [E+1] row segments of the experts
     int E, K, N;
+    int M;                   // EPI_WGRAD: columns of A (K is the expert's segment)
     void* out;               // EPI_GELU_H: [rows, N] dtype; EPI_STORE_F32: [rows, N] fp32
     // bf16 kernels: the EPI_GELU_H output and the EPI_STORE_F32 input A are h
     // in the tile layout of ffn_bf16.hip (h_tiled_rows rows); fp32 kernels:
     // row-major
+    float* out2;             // GELU'(a) [rows, N]: EPI_HGRAD output, EPI_DA input
 };
 // rows of the h tile layout for max_rows packed rows over E experts
 inline int64_t h_tiled_rows(int64_t max_rows, int64_t E) { return ((max_rows + 15 * E + 15) / 16) * 16; }
 hipError_t launch_ffn_gemm_bf16(const GemmArgs& g, int epi, int64_t max_rows, hipStream_t st);
+// The pipelined 256 x 256 bf16 kernel with explicit operand layouts (the
+// backward's expert GEMMs): A row-major (not the h tile layout); B as [E, K, N]
+// or, b_kc, [E, N, K] (then K must be a multiple of 32).  Returns false and
+// launches nothing when the problem is too small for it or outside its limits.
+bool launch_ffn_gemm_bf16_pipe(const GemmArgs& g, int epi, bool b_kc, int64_t max_rows, hipStream_t st,
+                               hipError_t* err);
 hipError_t launch_ffn_gemm_f32(const GemmArgs& g, int epi, hipStream_t st);
 
 // ---- combine.hip ----------------------------------------------------------

@@ -130,6 +130,14 @@ _add(MoEConfig("dense_soft_e16", T=4096, d=1024, E=16, k=16, d_ff=4096,
                capacity_factor=0.0, temperature=0.2,
                note="k = E: the soft MoE of every expert, 4096 rows each"))
 
+# long expert segments next to idle and one-row experts: the literal Zipf(1.2)
+# gate bias without a capacity limit gives 3 idle experts, several with 1-2
+# rows and the busiest with ~25k (the backward's weight-gradient GEMM runs
+# its pipelined form from 1024 rows per expert on average)
+_add(MoEConfig("long_segments", T=32768, d=1024, E=64, k=2, d_ff=1024,
+               capacity_factor=0.0, zipf_s=1.2, zipf_alpha=1.0,
+               note="idle, one-row and ~25k-row experts in one batch"))
+
 # limits of the library: E = 1024 experts, k = 32 choices per token
 _add(MoEConfig("max_experts", T=2048, d=64, E=1024, k=4, d_ff=64,
                capacity_factor=1.0, bias_std=0.1))

@@ -127,6 +127,49 @@ def test_backward_full_size(moe, orc, name):
     assert rs <= 1e-3 * (np.abs(got["dWg"]).max() + 1e-30) * np.sqrt(cfg.E)
 
 
+def test_backward_long_segments(moe, orc):
+    """Idle, one-row and long expert segments in one batch: exact zeros for
+    the idle experts, full weight gradients of the five least busy active
+    experts and of the two whose row counts are nearest 400, sampled dx and
+    the gate sums."""
+    cfg = get("long_segments")
+    H.log(f"[backward-long] T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} d_ff={cfg.d_ff}")
+    inp = make_inputs(cfg)
+    dy = dy_of(cfg)
+    got, L, counts, offsets = forward_backward(moe, cfg, inp, dy)
+    tol = TOL[cfg.dtype]
+    idx, w = orc.route(L, cfg.k, cfg.temperature)
+    dsp = orc.dispatch(idx, cfg.E, orc.capacity(cfg.T, cfg.E, cfg.k, cfg.capacity_factor))
+    assert np.array_equal(dsp["offsets"], offsets)
+    slot = dsp["slot"]
+    idle = np.nonzero(counts == 0)[0]
+    assert len(idle) > 0
+    for e in idle:
+        for n in ("dW1", "db1", "dW2", "db2"):
+            assert not got[n][e].any(), (n, e)
+    act = np.nonzero(counts > 0)[0]
+    order = act[np.argsort(counts[act], kind="stable")]
+    mid = act[np.argsort(np.abs(counts[act] - 400), kind="stable")[:2]]
+    for e in sorted(set(order[:5].tolist() + mid.tolist())):
+        tt, jj = np.nonzero((slot >= 0) & (idx == e))
+        _, _, dW1, db1, dW2, db2 = orc.ffn_backward_rows(tt.astype(np.int32), idx[tt, jj], w[tt, jj], inp["x"],
+                                                         inp["W1"], inp["b1"], inp["W2"], inp["b2"], dy, cfg.E)
+        for n, ref in (("dW1", dW1), ("db1", db1), ("dW2", dW2), ("db2", db2)):
+            H.assert_close_norm(got[n][e], ref[e], tol, f"long_segments {n}[{e}] ({counts[e]} rows)")
+    toks = H.sample_tokens(cfg.T, 64, seed=9)
+    tt, jj = np.nonzero(slot[toks] >= 0)
+    dw = np.zeros((len(toks), cfg.k))
+    dwr, dxp, *_ = orc.ffn_backward_rows(toks[tt].astype(np.int32), idx[toks[tt], jj], w[toks[tt], jj], inp["x"],
+                                         inp["W1"], inp["b1"], inp["W2"], inp["b2"], dy, cfg.E)
+    dw[tt, jj] = dwr
+    dx_ref = np.zeros((len(toks), cfg.d))
+    np.add.at(dx_ref, tt, dxp)
+    _, _, _, dxg = orc.route_backward(inp["x"][toks], inp["Wg"], idx[toks], w[toks], dw, cfg.temperature)
+    H.assert_close_norm(got["dx"][toks], dx_ref + dxg, tol, "long_segments dx (sampled)")
+    scale = np.abs(got["dbg"]).max() + 1e-30
+    assert abs(got["dbg"].sum()) <= 1e-3 * scale * np.sqrt(cfg.E)
+
+
 def test_backward_repeatable(moe):
     cfg = get("medium_bf16")
     inp = make_inputs(cfg)
