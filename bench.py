@@ -39,17 +39,26 @@ STAGE_KERNELS = {
     "hist": ("hist_kernel",),
     "scatter": ("scatter_kernel",),
     "gather": ("gather_kernel",),
-    "ffn1": ("ffn_gemm_", ", 0>(moe::GemmArgs)"),
-    "ffn2": ("ffn_gemm_", ", 1>(moe::GemmArgs)"),
+    # the forward's GEMMs only: the 128x128 kernel (last template argument
+    # the epilogue) and the pipelined one with the forward's operand layouts
+    # (the backward's instantiations use other epilogues or layouts)
+    "ffn1": (", 0>(moe::GemmArgs)", ", 0, false, false, false>(moe::GemmArgs)"),
+    "ffn2": (", 1>(moe::GemmArgs)", ", 1, true, false, false>(moe::GemmArgs)"),
     "combine": ("combine_kernel",),
 }
 
 
+# sources of the layer forward's kernels and their launches (the backward,
+# heat map and loss-variant files build none of them)
+FORWARD_SOURCES = ("combine.hip", "dispatch.hip", "ffn_bf16.hip", "ffn_fp32.hip", "ffn_sched.h", "lds_dma.h",
+                   "moe_api.hip", "moe_common.h", "moe_kernels.h", "route.hip", "route_mfma.hip")
+
+
 def kernel_source_hash() -> str:
-    """Hash of every kernel source: counter records taken from other sources
-    no longer describe the kernels that run."""
+    """Hash of the forward kernels' sources: counter records taken from other
+    sources no longer describe the kernels that run."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
+    for name in FORWARD_SOURCES:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -126,7 +135,7 @@ def cpu_baseline(cfg, inp, budget_s):
 def _stage_of(kernel: str):
     for stage, pats in STAGE_KERNELS.items():
         if stage.startswith("ffn"):
-            if all(p in kernel for p in pats):
+            if "ffn_gemm_" in kernel and any(kernel.endswith(p) for p in pats):
                 return stage
         elif any(p in kernel for p in pats):
             return stage
