@@ -285,9 +285,13 @@ __device__ __forceinline__ bf16x8_t bwm_frag(const uint16_t* s, int base, int la
 }
 
 template <int MODE, int EPI>
-__global__ __launch_bounds__(256) void bw_mfma_kernel(BwGemmArgs g) {
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][BWM_TILE];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BWM_TILE];
+__global__ __launch_bounds__(256, MODE == BW_TN ? 4 : 1) void bw_mfma_kernel(BwGemmArgs g) {
+    // TN: both operands [k][row] (smaller tiles), no item list in LDS, and
+    // four workgroups per CU (at most 128 registers a lane): its few K-steps
+    // per tile wait on global loads, which more resident workgroups cover
+    constexpr int TILE = MODE == BW_TN ? BWM_BK * BWM_LDM : BWM_TILE;
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][TILE];
     __shared__ int mt_pre[1025];
     __shared__ int scan_tmp[32];
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
