@@ -74,6 +74,8 @@ def parse():
                     help="budget of the oracle's expert-FFN sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured copy and library-GEMM reference rates")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -202,6 +204,51 @@ def load_traffic(workload: str, stage: str):
     if rec.get("kernel_source_hash") != kernel_source_hash():
         return None
     return rec.get("bytes_per_launch")
+
+
+def measured_peaks(cfg, S, active, dev):
+    """What this GPU reaches on plain references, beside the published
+    peaks: a device-to-device copy of 1 GiB (HBM read + write), the vendor
+    library's bf16 GEMM (hipBLASLt through torch.matmul) on 8192^3, and the
+    same library on the workload's expert GEMM1 shape with the kept rows
+    spread evenly over the active experts (torch.bmm, contiguous operands,
+    no routing, no skew, no bias or GELU).  Reference rates only."""
+    import torch
+
+    def timed(fn, reps):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    out = {}
+    src = torch.empty(COPY_CALIB_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    t = timed(lambda: dst.copy_(src), 5)
+    out["copy_GB/s"] = 2 * COPY_CALIB_BYTES / t / 1e9
+    del src, dst
+    n = 8192
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    t = timed(lambda: torch.matmul(a, b), 5)
+    out["library_gemm_bf16_8192_TFLOP/s"] = 2 * n ** 3 / t / 1e12
+    del a, b
+    if cfg.dtype == "bf16" and active > 0:
+        m = (S + active - 1) // active
+        a = torch.randn(active, m, cfg.d, device=dev, dtype=torch.bfloat16)
+        b = torch.randn(active, cfg.d, cfg.d_ff, device=dev, dtype=torch.bfloat16)
+        t = timed(lambda: torch.bmm(a, b), 5)
+        out["library_bmm_expert_shape"] = f"{active} x [{m} x {cfg.d}] x [{cfg.d} x {cfg.d_ff}]"
+        out["library_bmm_expert_shape_TFLOP/s"] = 2.0 * active * m * cfg.d * cfg.d_ff / t / 1e12
+        del a, b
+    torch.cuda.empty_cache()
+    return out
 
 
 def time_heat_map(moe, s, cfg, d, y, counts, aux, ws, stream, reps=20):
@@ -459,6 +506,8 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         out["copy_calib_bytes"] = COPY_CALIB_BYTES
+    if not args.no_peaks and not args.copy_calib:
+        out["measured_peaks"] = measured_peaks(cfg, S, active, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
     print(json.dumps(out), flush=True)
