@@ -137,9 +137,16 @@ __device__ __forceinline__ void topk_group(const float* row, int E, int k, float
     }
 }
 
-template <int EP2, int BM, int NS, int KS>
-__global__ __launch_bounds__(256) void route_mfma_kernel(RouteArgs a, const uint16_t* __restrict__ W3) {
+// NW = 4 or 8 waves.  With 8, waves w and w + 4 cover the same logits and
+// split every stage's K-steps (group w / 4 takes the K-steps q with
+// q % 2 == w / 4); their fp32 partial sums are added once at the end, group
+// 0's plus group 1's, in that order.  Two waves per SIMD then hide each
+// other's LDS and MFMA latencies.
+template <int EP2, int BM, int NS, int KS, int NW = 4>
+__global__ __launch_bounds__(64 * NW) void route_mfma_kernel(RouteArgs a, const uint16_t* __restrict__ W3) {
+    static_assert(NW == 4 || (NW == 8 && KS % 2 == 0), "four waves, or eight splitting an even K-step count");
     constexpr int BKG = 32;
+    constexpr int KQ = NW / 4;                          // wave groups splitting K
     constexpr int WN = EP2 / 16 >= 4 ? 4 : EP2 / 16;  // waves across experts
     constexpr int WM = 4 / WN;                          // waves across tokens
     constexpr int NBW = EP2 / 16 / WN;                  // 16-expert blocks per wave
@@ -148,8 +155,8 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(RouteArgs a, const uint
     constexpr int ROWS = BM + 3 * EP2;       // 64-byte rows per K-step: tokens, then weight parts
     constexpr int INSTR1 = ROWS / 16;        // 1 KiB wave loads per K-step
     constexpr int INSTR = KS * INSTR1;       // per stage of KS K-steps
-    constexpr int PER = (INSTR + 3) / 4;     // per wave; the ones past INSTR fill unused rows
-    constexpr int STAGE = 4 * PER * 512;     // bf16 elements per slot
+    constexpr int PER = (INSTR + NW - 1) / NW;   // per wave; the ones past INSTR fill unused rows
+    constexpr int STAGE = NW * PER * 512;    // bf16 elements per slot
     constexpr int LTP = EP2 + 1;
     static_assert(BM % 16 == 0, "token rows in whole wave loads");
     static_assert((NS - 2) * PER < 64, "vmcnt range");
@@ -164,7 +171,8 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(RouteArgs a, const uint
     const int64_t t0 = (int64_t)blockIdx.x * BM;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wid / WN, wn = wid % WN;
+    const int wq = wid / 4, wl = wid % 4;   // K group, and the wave's logits block
+    const int wm = wl / WN, wn = wl % WN;
     const int g16 = lane >> 4, i16 = lane & 15;
     const int nk = (d + BKG - 1) / BKG;          // K-steps
     const int nst = (nk + KS - 1) / KS;          // stages
@@ -210,10 +218,12 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(RouteArgs a, const uint
         dma_barrier<(NS - 2) * PER>();
         issue(st + NS - 1, slot == 0 ? NS - 1 : slot - 1);
         const uint16_t* sp = sm.ring[slot];
-        // every fragment of the stage first, then the MFMAs
+        // every fragment of the stage first, then the MFMAs (this wave's
+        // K-steps of the stage only)
         bf16x8_t xf[KS][MBW], wf[KS][3][NBW];
 #pragma unroll
         for (int q = 0; q < KS; ++q) {
+            if (q % KQ != wq) continue;
             const uint16_t* sq = sp + q * INSTR1 * 512;
 #pragma unroll
             for (int mb = 0; mb < MBW; ++mb)
@@ -226,7 +236,8 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(RouteArgs a, const uint
                         &sq[k64_slot(BM + s * EP2 + (wn * NBW + nb) * 16 + i16, g16) * 8]);
         }
 #pragma unroll
-        for (int q = 0; q < KS; ++q)
+        for (int q = 0; q < KS; ++q) {
+            if (q % KQ != wq) continue;
 #pragma unroll
             for (int s = 0; s < 3; ++s)
 #pragma unroll
@@ -235,29 +246,40 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(RouteArgs a, const uint
                     for (int mb = 0; mb < MBW; ++mb)
                         acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[q][s][nb], xf[q][mb], acc[mb][nb],
                                                                                0, 0, 0);
+        }
         slot = slot + 1 == NS ? 0 : slot + 1;
     }
     // the trailing out-of-range loads still write the ring, which the logit
     // tile overlays
     dma_barrier<0>();
 
-    // logits (+ bias) -> LDS tile [BM][EP2]
+    // logits (+ bias) -> LDS tile [BM][EP2]; with two K groups, group 1 puts
+    // its partial sums there first and group 0 adds its own to them
+    for (int g = KQ - 1; g >= 0; --g) {
+        if (wq == g) {
 #pragma unroll
-    for (int mb = 0; mb < MBW; ++mb) {
-        const int tl = (wm * MBW + mb) * 16 + i16;
+            for (int mb = 0; mb < MBW; ++mb) {
+                const int tl = (wm * MBW + mb) * 16 + i16;
 #pragma unroll
-        for (int nb = 0; nb < NBW; ++nb) {
+                for (int nb = 0; nb < NBW; ++nb) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int e = (wn * NBW + nb) * 16 + 4 * g16 + q;
-                const float b = (a.bg != nullptr && e < E) ? a.bg[e] : 0.0f;
-                sm.lt[tl * LTP + e] = acc[mb][nb][q] + b;
+                    for (int q = 0; q < 4; ++q) {
+                        const int e = (wn * NBW + nb) * 16 + 4 * g16 + q;
+                        if (g > 0) {
+                            sm.lt[tl * LTP + e] = acc[mb][nb][q];
+                        } else {
+                            const float b = (a.bg != nullptr && e < E) ? a.bg[e] : 0.0f;
+                            const float v = KQ > 1 ? acc[mb][nb][q] + sm.lt[tl * LTP + e] : acc[mb][nb][q];
+                            sm.lt[tl * LTP + e] = v + b;
+                        }
+                    }
+                }
             }
         }
+        __syncthreads();
     }
-    __syncthreads();
     if (a.logits != nullptr) {
-        for (int i = tid; i < BM * E; i += 256) {
+        for (int i = tid; i < BM * E; i += 64 * NW) {
             const int tl = i / E, e = i - tl * E;
             if (t0 + tl < T) a.logits[(t0 + tl) * E + e] = sm.lt[tl * LTP + e];
         }
@@ -266,7 +288,7 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(RouteArgs a, const uint
     constexpr int NV = EP2 / G;
     constexpr int GPW = 64 / G;   // tokens per wave per pass
     const int gl = lane & (G - 1), gi = lane / G;
-    for (int base = wid * GPW; base < BM; base += 4 * GPW) {
+    for (int base = wid * GPW; base < BM; base += NW * GPW) {
         const int tl = base + gi;
         const int64_t t = t0 + tl;
         const bool active = tl < BM && t < T;
@@ -292,16 +314,20 @@ bool route_mfma_supported(int dtype, int E, int k) {
 
 size_t route_mfma_ws_bytes(int d, int E) { return (size_t)3 * d * route_mfma_ep2(E) * sizeof(uint16_t); }
 
-template <int EP2, int BM, int NS, int KS>
+template <int EP2, int BM, int NS, int KS, int NW = 4>
 static void launch_bm(const RouteArgs& a, const uint16_t* W3, hipStream_t st) {
     const dim3 grid((unsigned)((a.T + BM - 1) / BM));
-    hipLaunchKernelGGL((route_mfma_kernel<EP2, BM, NS, KS>), grid, dim3(256), 0, st, a, W3);
+    hipLaunchKernelGGL((route_mfma_kernel<EP2, BM, NS, KS, NW>), grid, dim3(64 * NW), 0, st, a, W3);
 }
 
 // Tile choice per expert width.  Up to 128 experts: 32- or 64-token tiles,
 // two K-steps per stage (one barrier and one batch of LDS reads per 64 of
 // K), ring of 4 slots (3 of 52 KiB for 128 experts).  256 experts: 128-token tiles halve the re-reads
 // of the 3 MiB weight split per token; one K-step per stage, 2 slots.
+#ifndef MOE_ROUTE_NW
+#define MOE_ROUTE_NW 8   // waves per workgroup up to 64 experts
+#endif
+
 template <int EP2>
 static void launch_ep2(const RouteArgs& a, const uint16_t* W3, int cus, hipStream_t st) {
     constexpr int WM = 4 / (EP2 / 16 >= 4 ? 4 : EP2 / 16);
@@ -311,11 +337,11 @@ static void launch_ep2(const RouteArgs& a, const uint16_t* W3, int cus, hipStrea
     } else if constexpr (EP2 == 128) {
         launch_bm<128, 32, 3, 2>(a, W3, st);
     } else if constexpr (16 * WM > 32) {
-        launch_bm<EP2, 64, 4, 2>(a, W3, st);
+        launch_bm<EP2, 64, 4, 2, MOE_ROUTE_NW>(a, W3, st);
     } else {
         // 64-token tiles halve the weight traffic per token once they still fill the CUs
-        if ((a.T + 63) / 64 >= cus) launch_bm<EP2, 64, 4, 2>(a, W3, st);
-        else launch_bm<EP2, 32, 4, 2>(a, W3, st);
+        if ((a.T + 63) / 64 >= cus) launch_bm<EP2, 64, 4, 2, MOE_ROUTE_NW>(a, W3, st);
+        else launch_bm<EP2, 32, 4, 2, MOE_ROUTE_NW>(a, W3, st);
     }
 }
 
