@@ -92,7 +92,7 @@ static int validate(const moe_shape* s, Geo* g) {
         g->cap = capacity_of(s->T, s->E, s->k, s->capacity_factor);
         g->max_rows = std::min(s->T * s->k, s->E * g->cap);
         g->esz = s->dtype == MOE_BF16 ? 2 : 4;
-        g->BT = dispatch_block_tokens((int)s->E);
+        g->BT = dispatch_block_tokens(s->T, (int)s->E, (int)s->k);
         g->nblk = (int)((s->T + g->BT - 1) / g->BT);
         g->mfma_gate = route_mfma_supported(s->dtype, (int)s->E, (int)s->k);
     }

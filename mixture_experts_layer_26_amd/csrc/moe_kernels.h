@@ -52,7 +52,7 @@ struct DispatchArgs {
     void* x_perm;          // [max_rows, d]
     int64_t row_bytes;     // d * element size
 };
-int dispatch_block_tokens(int E);
+int dispatch_block_tokens(int64_t T, int E, int k);
 hipError_t launch_hist(const DispatchArgs& a, hipStream_t st);
 hipError_t launch_scatter(const DispatchArgs& a, hipStream_t st);
 hipError_t launch_gather(const DispatchArgs& a, hipStream_t st);

@@ -20,7 +20,7 @@
 // through a ring of NS slots, so NS-1 stages of loads are in flight; both
 // operands are read back with ds_read_b128 from the same swizzled layout.  The four waves split the
 // expert columns (and the token rows when EP2 < 64).  The logit tile goes to
-// LDS, then groups of G = min(16, EP2/4) lanes select the top k of each
+// LDS, then groups of 16 lanes (one DPP row) select the top k of each
 // token with arg-max reductions over DPP lane moves.
 #include "lds_dma.h"
 #include "moe_kernels.h"
@@ -284,7 +284,9 @@ __global__ __launch_bounds__(64 * NW) void route_mfma_kernel(RouteArgs a, const 
             if (t0 + tl < T) a.logits[(t0 + tl) * E + e] = sm.lt[tl * LTP + e];
         }
     }
-    constexpr int G = EP2 / 4 > 16 ? 16 : EP2 / 4;
+    // one DPP row of 16 lanes per token, whatever the expert count: k up to
+    // 16 winners (k = E for the dense soft layer of 16 experts)
+    constexpr int G = 16;
     constexpr int NV = EP2 / G;
     constexpr int GPW = 64 / G;   // tokens per wave per pass
     const int gl = lane & (G - 1), gi = lane / G;
@@ -305,11 +307,9 @@ int route_mfma_ep2(int E) {
     return e;
 }
 
-// the top-k groups have EP2/4 lanes (at most 16) and lane j keeps the j-th pick
+// the top-k groups have 16 lanes and lane j keeps the j-th pick
 bool route_mfma_supported(int dtype, int E, int k) {
-    const int ep2 = route_mfma_ep2(E);
-    const int g = ep2 / 4 > 16 ? 16 : ep2 / 4;
-    return dtype == MOE_BF16 && E <= 256 && k <= g;
+    return dtype == MOE_BF16 && E <= 256 && k <= 16;
 }
 
 size_t route_mfma_ws_bytes(int d, int E) { return (size_t)3 * d * route_mfma_ep2(E) * sizeof(uint16_t); }

@@ -110,6 +110,13 @@ _add(MoEConfig("one_expert", T=300, d=96, E=1, k=1, d_ff=160,
                capacity_factor=0.0, bias_std=0.1))
 _add(MoEConfig("k_equals_e", T=300, d=64, E=4, k=4, d_ff=128,
                capacity_factor=0.0, temperature=0.5, bias_std=0.1))
+# the matrix-core router with up to 16 winners per token: k = E on 12
+# experts (every expert, ragged d) and k = 16 of 40 experts (4 logits per lane)
+_add(MoEConfig("soft_k_equals_e12", T=1000, d=200, E=12, k=12, d_ff=136,
+               capacity_factor=0.0, temperature=0.2, bias_std=0.1,
+               gate_bias_std=0.3))
+_add(MoEConfig("k16_e40", T=777, d=136, E=40, k=16, d_ff=200,
+               capacity_factor=1.5, temperature=0.7, bias_std=0.1))
 _add(MoEConfig("cap_one", T=200, d=64, E=8, k=2, d_ff=64,
                capacity_factor=0.02, bias_std=0.1,
                note="capacity clips to 1 slot per expert"))
