@@ -137,18 +137,21 @@ __device__ __forceinline__ void topk_group(const float* row, int E, int k, float
     }
 }
 
-// NW = 4 or 8 waves.  With 8, waves w and w + 4 cover the same logits and
-// split every stage's K-steps (group w / 4 takes the K-steps q with
-// q % 2 == w / 4); their fp32 partial sums are added once at the end, group
-// 0's plus group 1's, in that order.  Two waves per SIMD then hide each
-// other's LDS and MFMA latencies.
-template <int EP2, int BM, int NS, int KS, int NW = 4>
+// NW = 4 or 8 waves.  With 8 and SE = false, waves w and w + 4 cover the
+// same logits and split every stage's K-steps (group w / 4 takes the
+// K-steps q with q % 2 == w / 4); their fp32 partial sums are added once at
+// the end, group 0's plus group 1's, in that order.  With 8 and SE = true
+// (128 experts or more) the eight waves split the experts instead.  Either
+// way two waves per SIMD hide each other's LDS and MFMA latencies.
+template <int EP2, int BM, int NS, int KS, int NW = 4, bool SE = false>
 __global__ __launch_bounds__(64 * NW) void route_mfma_kernel(RouteArgs a, const uint16_t* __restrict__ W3) {
-    static_assert(NW == 4 || (NW == 8 && KS % 2 == 0), "four waves, or eight splitting an even K-step count");
+    static_assert(NW == 4 || (NW == 8 && (SE || KS % 2 == 0)),
+                  "four waves, or eight splitting the experts or an even K-step count");
+    static_assert(!SE || (NW == 8 && EP2 >= 128), "expert split: eight waves of 16-expert blocks");
     constexpr int BKG = 32;
-    constexpr int KQ = NW / 4;                          // wave groups splitting K
-    constexpr int WN = EP2 / 16 >= 4 ? 4 : EP2 / 16;  // waves across experts
-    constexpr int WM = 4 / WN;                          // waves across tokens
+    constexpr int KQ = SE ? 1 : NW / 4;                 // wave groups splitting K
+    constexpr int WN = SE ? 8 : EP2 / 16 >= 4 ? 4 : EP2 / 16;   // waves across experts
+    constexpr int WM = (SE ? 8 : 4) / WN;               // waves across tokens
     constexpr int NBW = EP2 / 16 / WN;                  // 16-expert blocks per wave
     constexpr int MBW = BM / 16 / WM;                   // 16-token blocks per wave
     static_assert(MBW >= 1 && NBW >= 1, "tile too small for four waves");
@@ -171,7 +174,7 @@ __global__ __launch_bounds__(64 * NW) void route_mfma_kernel(RouteArgs a, const 
     const int64_t t0 = (int64_t)blockIdx.x * BM;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wq = wid / 4, wl = wid % 4;   // K group, and the wave's logits block
+    const int wq = SE ? 0 : wid / 4, wl = SE ? wid : wid % 4;   // K group, and the wave's logits block
     const int wm = wl / WN, wn = wl % WN;
     const int g16 = lane >> 4, i16 = lane & 15;
     const int nk = (d + BKG - 1) / BKG;          // K-steps
@@ -314,16 +317,20 @@ bool route_mfma_supported(int dtype, int E, int k) {
 
 size_t route_mfma_ws_bytes(int d, int E) { return (size_t)3 * d * route_mfma_ep2(E) * sizeof(uint16_t); }
 
-template <int EP2, int BM, int NS, int KS, int NW = 4>
+template <int EP2, int BM, int NS, int KS, int NW = 4, bool SE = false>
 static void launch_bm(const RouteArgs& a, const uint16_t* W3, hipStream_t st) {
     const dim3 grid((unsigned)((a.T + BM - 1) / BM));
-    hipLaunchKernelGGL((route_mfma_kernel<EP2, BM, NS, KS, NW>), grid, dim3(64 * NW), 0, st, a, W3);
+    hipLaunchKernelGGL((route_mfma_kernel<EP2, BM, NS, KS, NW, SE>), grid, dim3(64 * NW), 0, st, a, W3);
 }
 
-// Tile choice per expert width.  Up to 128 experts: 32- or 64-token tiles,
+// Tile choice per expert width.  Up to 64 experts: 32- or 64-token tiles,
 // two K-steps per stage (one barrier and one batch of LDS reads per 64 of
-// K), ring of 4 slots (3 of 52 KiB for 128 experts).  256 experts: 128-token tiles halve the re-reads
-// of the 3 MiB weight split per token; one K-step per stage, 2 slots.
+// K), ring of 4 slots.  128 experts: 32-token tiles, one K-step per stage,
+// 4 slots of 32 KiB, eight waves splitting the experts.  256 experts:
+// 128-token tiles halve the re-reads of the 3 MiB weight split per token;
+// one K-step per stage, 2 slots, eight waves splitting the experts (with
+// four, one wave per SIMD, the workload of 256 experts and 32768 tokens took
+// 241 us instead of 161; 128 experts and 8192 tokens 42 instead of 36).
 #ifndef MOE_ROUTE_NW
 #define MOE_ROUTE_NW 8   // waves per workgroup up to 64 experts
 #endif
@@ -332,10 +339,10 @@ template <int EP2>
 static void launch_ep2(const RouteArgs& a, const uint16_t* W3, int cus, hipStream_t st) {
     constexpr int WM = 4 / (EP2 / 16 >= 4 ? 4 : EP2 / 16);
     if constexpr (EP2 == 256) {
-        if ((a.T + 127) / 128 >= cus) launch_bm<256, 128, 2, 1>(a, W3, st);
+        if ((a.T + 127) / 128 >= cus) launch_bm<256, 128, 2, 1, 8, true>(a, W3, st);
         else launch_bm<256, 64, 3, 1>(a, W3, st);
     } else if constexpr (EP2 == 128) {
-        launch_bm<128, 32, 3, 2>(a, W3, st);
+        launch_bm<128, 32, 4, 1, 8, true>(a, W3, st);
     } else if constexpr (16 * WM > 32) {
         launch_bm<EP2, 64, 4, 2, MOE_ROUTE_NW>(a, W3, st);
     } else {
