@@ -85,6 +85,17 @@ def parse():
     return ap.parse_args()
 
 
+def dispatch_block_tokens(T, E, k):
+    """Tokens per histogram/scatter block, the library's rule: 1024 (512 above
+    256 experts, 256 above 512), halved while a block holds more than 2048
+    slots and the block count stays <= 256 (only the reported bytes of the
+    two dispatch launches depend on it)."""
+    bt = 1024 if E <= 256 else 512 if E <= 512 else 256
+    while bt > 64 and bt * k > 2048 and (T + bt // 2 - 1) // (bt // 2) <= 256:
+        bt //= 2
+    return bt
+
+
 def stage_bytes_flops(cfg, S, active, esz, nblk):
     """Algorithmic bytes and FLOPs of each launch (what the method must move
     or compute over the kept slots; no dense T x E work)."""
@@ -93,7 +104,9 @@ def stage_bytes_flops(cfg, S, active, esz, nblk):
         "route": (T * d * esz + d * E * 4 + T * k * 8, 2 * T * d * E),
         "hist": (T * k * 4 + nblk * E * 4, 0),
         "scatter": (nblk * nblk * E * 4 + T * k * 12 + S * 8, 0),
-        "gather": (2 * S * d * esz, 0),
+        # every token row read once (its k copies come from cache), every
+        # kept row written once, plus the permutation
+        "gather": (T * d * esz + S * d * esz + S * 4, 0),
         "ffn1": (active * d * F * esz + S * d * esz + S * F * esz + active * F * 4, 2 * S * d * F),
         "ffn2": (active * F * d * esz + S * F * esz + S * d * 4 + active * d * 4, 2 * S * d * F),
         "combine": (S * d * 4 + T * d * 4 + T * k * 8, 2 * S * d),
@@ -444,8 +457,7 @@ def main():
     rt = routed.cpu().numpy()
     S = int(c.sum())
     active = int((c > 0).sum())
-    nblk = (cfg.T + (1024 if cfg.E <= 256 else 512 if cfg.E <= 512 else 256) - 1) // \
-        (1024 if cfg.E <= 256 else 512 if cfg.E <= 512 else 256)
+    nblk = (cfg.T + dispatch_block_tokens(cfg.T, cfg.E, cfg.k) - 1) // dispatch_block_tokens(cfg.T, cfg.E, cfg.k)
     bf = stage_bytes_flops(cfg, S, active, esz, nblk)
     ffn_flops = 4 * S * cfg.d * cfg.d_ff
     gemm_us = stage_us["ffn1"] + stage_us["ffn2"]
@@ -489,6 +501,13 @@ def main():
         "grouped_gemm": {"tflops": ffn_flops / (gemm_us * 1e-6) / 1e12,
                          "frac_peak_bf16": ffn_flops / (gemm_us * 1e-6) / peak_mm, "us": gemm_us},
         "stages_us": stage_us,
+        # algorithmic bytes of the routing, permutation and combine launches
+        # over their HIP-event times (which include the event records: a few
+        # us on these short launches, see the kernel trace in profiles/)
+        "stage_hbm": {n: {"us": stage_us[n], "algorithmic_bytes": bf[n][0],
+                          "GB/s": bf[n][0] / (stage_us[n] * 1e-6) / 1e9,
+                          "frac_hbm": bf[n][0] / (stage_us[n] * 1e-6) / PEAK_HBM}
+                      for n in ("route", "hist", "scatter", "gather", "combine") if n in stage_us},
         "layer_tflops": (ffn_flops + 2 * cfg.T * cfg.d * cfg.E) / (ms * 1e-3) / 1e12,
         "kept_slots": S, "dropped_slots": cfg.T * cfg.k - S, "active_experts": active,
         "routed_cv": float(rt.std() / rt.mean()),
