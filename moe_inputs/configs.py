@@ -117,6 +117,14 @@ _add(MoEConfig("soft_k_equals_e12", T=1000, d=200, E=12, k=12, d_ff=136,
                gate_bias_std=0.3))
 _add(MoEConfig("k16_e40", T=777, d=136, E=40, k=16, d_ff=200,
                capacity_factor=1.5, temperature=0.7, bias_std=0.1))
+# the router's eight-wave expert split: 100 experts (padded to 128), and
+# 200 experts (padded to 256) over enough tokens for its 128-token tiles,
+# with a ragged last tile
+_add(MoEConfig("e100_k5", T=1500, d=256, E=100, k=5, d_ff=200,
+               capacity_factor=1.3, temperature=0.8, bias_std=0.1,
+               gate_bias_std=0.3))
+_add(MoEConfig("e200_t33001", T=33001, d=64, E=200, k=2, d_ff=64,
+               capacity_factor=1.1, bias_std=0.1, gate_bias_std=0.3))
 _add(MoEConfig("cap_one", T=200, d=64, E=8, k=2, d_ff=64,
                capacity_factor=0.02, bias_std=0.1,
                note="capacity clips to 1 slot per expert"))

@@ -20,7 +20,8 @@ pytestmark = pytest.mark.gpu
 
 SMALL = ["tiny_fp32", "tiny_fp32_bias", "ragged_bf16", "ragged_fp32", "medium_bf16",
          "hybrid_small", "clustered_small", "single_token", "one_expert", "k_equals_e",
-         "cap_one", "max_experts", "max_k", "soft_k_equals_e12", "k16_e40"]
+         "cap_one", "max_experts", "max_k", "soft_k_equals_e12", "k16_e40", "e100_k5",
+         "e200_t33001"]
 FULL = ["bf16_e16", "skewed_e64", "skewed_e64_literal", "hybrid_e128", "large_e256", "dense_soft_e16", "ragged_large",
         "ragged_large_even"]
 FULL_Y = {"bf16_e16"}          # oracle over every token still takes seconds
