@@ -38,12 +38,15 @@ STAGE_KERNELS = {
     "route": ("route_mfma_kernel", "gate_topk_kernel"),
     "hist": ("hist_kernel",),
     "scatter": ("scatter_kernel",),
-    "gather": ("gather_kernel",),
-    # the forward's GEMMs only: the 128x128 kernel (last template argument
-    # the epilogue) and the pipelined one with the forward's operand layouts
-    # (the backward's instantiations use other epilogues or layouts)
-    "ffn1": (", 0>(moe::GemmArgs)", ", 0, false, false, false>(moe::GemmArgs)"),
-    "ffn2": (", 1>(moe::GemmArgs)", ", 1, true, false, false>(moe::GemmArgs)"),
+    "gather": ("gather_kernel", "gather_tiled_kernel"),
+    # the forward's GEMMs only: the 128x128 kernel (template arguments end
+    # with the epilogue and the A layout) and the pipelined one with the
+    # forward's operand layouts (the backward's instantiations use other
+    # epilogues or layouts); GEMM1 reads x_perm row-major (moe_grouped_ffn)
+    # or tiled (moe_layer_forward)
+    "ffn1": (", 0, false>(moe::GemmArgs)", ", 0, true>(moe::GemmArgs)",
+             ", 0, false, false, false>(moe::GemmArgs)", ", 0, true, false, false>(moe::GemmArgs)"),
+    "ffn2": (", 1, true>(moe::GemmArgs)", ", 1, true, false, false>(moe::GemmArgs)"),
     "combine": ("combine_kernel",),
 }
 
@@ -367,8 +370,9 @@ def time_backward(moe, s, cfg, d, ws, stream, reps=5):
 
     slot = region(moe.MOE_WS_SLOT, i32, T * k, 4)
     offsets = region(moe.MOE_WS_OFFSETS, i32, E + 1, 4)
-    xperm = region(moe.MOE_WS_XPERM, torch.int16 if cfg.dtype == "bf16" else f32, R * D,
-                   2 if cfg.dtype == "bf16" else 4)
+    # a bf16 forward keeps x_perm only in the tile layout: the backward copies
+    # the rows itself (its time includes that copy)
+    xperm = None if cfg.dtype == "bf16" else region(moe.MOE_WS_XPERM, f32, R * D, 4)
     outp = region(moe.MOE_WS_OUT, f32, R * D, 4)
     dy = torch.from_numpy(np.random.default_rng(77).standard_normal((T, D)).astype(np.float32)).to(dev)
     g = [torch.empty(sh, dtype=f32, device=dev) for sh in ((T, D), (D, E), (E,), (E, D, F), (E, F), (E, F, D), (E, D))]

@@ -116,7 +116,11 @@ size_t moe_workspace_size(const moe_shape* s);
 /* Byte offset inside the workspace of an intermediate that
  * moe_layer_forward leaves there, for inspection after the call completes:
  * which = MOE_WS_PERM (int32 [max_rows]), MOE_WS_SLOT (int32 [T,k]),
- * MOE_WS_OFFSETS (int32 [E+1]), MOE_WS_XPERM (dtype [max_rows,d]),
+ * MOE_WS_OFFSETS (int32 [E+1]), MOE_WS_XPERM (dtype [max_rows,d]; fp32
+ * layers only -- a bf16 layer's forward keeps x_perm only as MOE_WS_XPT),
+ * MOE_WS_XPT (bf16 layers: x_perm in the tile layout of MOE_WS_H below with
+ * ceil(d/32) column tiles, the first GEMM's operand; padding rows and columns
+ * d..32*ceil(d/32)-1 are zero),
  * MOE_WS_H (h; fp32 layers: [max_rows,d_ff] row-major; bf16 layers: 16-row x
  * 32-column tiles over expert segments that start at multiples of 16 rows --
  * expert e's local row i is padded row p = P[e] + i with P[e] the sum of the
@@ -126,7 +130,7 @@ size_t moe_workspace_size(const moe_shape* s);
  * [max_rows,d], the expert outputs before the weighted sum).  -1 if
  * invalid. */
 enum { MOE_WS_PERM = 0, MOE_WS_SLOT = 1, MOE_WS_OFFSETS = 2, MOE_WS_XPERM = 3, MOE_WS_H = 4,
-       MOE_WS_OUT = 5 };
+       MOE_WS_OUT = 5, MOE_WS_XPT = 6 };
 int64_t moe_workspace_offset(const moe_shape* s, int which);
 
 const char* moe_status_string(int status);
@@ -276,11 +280,14 @@ int moe_layer_forward(const moe_shape* s, const void* x, const float* Wg, const 
  * that received no row get zero weight and bias gradients ([EP] section
  * 4.3, expert-grained gradients).
  * Inputs from the forward call: topk_idx, topk_w, slot, offsets, x_perm
- * (dtype [max_rows,d]) and out_perm (fp32 [max_rows,d], the expert outputs
- * before the weighted sum) -- the outputs of moe_route / moe_dispatch /
- * moe_grouped_ffn, or the regions MOE_WS_SLOT, MOE_WS_OFFSETS,
- * MOE_WS_XPERM, MOE_WS_OUT of a moe_layer_forward workspace (pass the
- * forward's topk_idx and topk_w outputs).  dy [T,d] fp32.
+ * (dtype [max_rows,d], or NULL: the kept rows of x are then copied by slot
+ * into this call's workspace) and out_perm (fp32 [max_rows,d], the expert
+ * outputs before the weighted sum) -- the outputs of moe_route /
+ * moe_dispatch / moe_grouped_ffn, or the regions MOE_WS_SLOT,
+ * MOE_WS_OFFSETS, MOE_WS_OUT of a moe_layer_forward workspace with x_perm
+ * = MOE_WS_XPERM (fp32 layers) or NULL (bf16 layers, whose forward keeps
+ * x_perm only in the tile layout); pass the forward's topk_idx and topk_w
+ * outputs.  dy [T,d] fp32.
  * Outputs (fp32, overwritten): dx [T,d], dWg [d,E], dbg [E], dW1
  * [E,d,d_ff], db1 [E,d_ff], dW2 [E,d_ff,d], db2 [E,d].
  * Arithmetic: fp32 on the vector ALUs; bf16 operands are widened exactly;

@@ -27,7 +27,7 @@ if not os.path.exists(LIB_PATH):
 _lib = C.CDLL(LIB_PATH)
 
 MOE_F32, MOE_BF16 = 0, 1
-MOE_WS_PERM, MOE_WS_SLOT, MOE_WS_OFFSETS, MOE_WS_XPERM, MOE_WS_H, MOE_WS_OUT = range(6)
+MOE_WS_PERM, MOE_WS_SLOT, MOE_WS_OFFSETS, MOE_WS_XPERM, MOE_WS_H, MOE_WS_OUT, MOE_WS_XPT = range(7)
 MOE_ROUTER_TOPK, MOE_ROUTER_TOP1_FULL = 0, 1
 MOE_LOSS_SHARE, MOE_LOSS_VARIANCE = 0, 1
 

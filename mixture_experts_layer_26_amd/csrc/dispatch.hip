@@ -18,6 +18,7 @@
 //             loss ([EP] section 2.3);
 //   gather  : x_perm[row] = x[perm[row]] with 16-byte vector copies, one
 //             wave per row; pads perm with -1 past the used rows.
+#include "ffn_sched.h"
 #include "moe_common.h"
 #include "moe_kernels.h"
 
@@ -155,6 +156,133 @@ __global__ __launch_bounds__(256) void gather_kernel(DispatchArgs a) {
             a.perm[r] = -1;
         }
     }
+}
+
+// The fused bf16 forward's copy: x_perm[row] = x[perm[row]] in the grouped
+// GEMM's 16-row x 32-column tile layout over expert segments
+// padded to 16 rows (padded row p, column c at ((p / 16) KT + c / 32) 512 +
+// (p % 16) 32 + c % 32, KT = ceil(d / 32)).  In that layout one K-step of 16
+// rows of GEMM1's activation operand is one contiguous KiB: a global -> LDS
+// load of 64-byte row pieces moves half as many bytes per cycle as one of
+// contiguous KiBs.  Padding rows and columns d .. 32 KT - 1 are written as
+// zeros (the weight rows past d are zero, so the K tail must be finite).
+// One workgroup per 16-row block (one expert: segments are padded to 16),
+// in column spans of 1024: each wave reads whole rows (contiguous KiBs) into
+// an LDS block, then the span's tiles are written, one contiguous KiB per
+// wave instruction.  (The row-major x_perm is not written.)
+__global__ __launch_bounds__(256) void gather_tiled_kernel(DispatchArgs a, uint16_t* __restrict__ x_pt, int d) {
+    constexpr int SPAN = 1024;        // columns per pass
+    constexpr int LROW = SPAN + 32;   // LDS row stride: rows 64 bytes apart on the banks
+    __shared__ int s_off[1025];
+    __shared__ int s_poff[1025];
+    __shared__ int scan_tmp[32];
+    __shared__ int s_src[16];
+    __shared__ __attribute__((aligned(16))) uint16_t buf[16 * LROW];
+    const int E = a.E;
+    for (int i = threadIdx.x; i <= E; i += blockDim.x) s_off[i] = a.offsets[i];
+    __syncthreads();
+    build_padded_offsets(s_off, E, s_poff, scan_tmp);   // ends with a barrier
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wid = threadIdx.x / kWave;
+    const int KT = (d + 31) >> 5;
+    const int dpad = KT * 32;
+    const int nblk16 = s_poff[E] >> 4;
+    const uint4* __restrict__ x4 = static_cast<const uint4*>(a.x);
+    uint4* __restrict__ t4 = reinterpret_cast<uint4*>(x_pt);
+    const int64_t d16 = d / 8;   // 16-byte chunks per row (d is a multiple of 8)
+    for (int pb = blockIdx.x; pb < nblk16; pb += gridDim.x) {
+        if (threadIdx.x < 16) {
+            const int p = (pb << 4) + threadIdx.x;
+            int lo = 0, hi = E;   // largest e with s_poff[e] <= p: the expert holding the block
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (s_poff[mid] <= p) lo = mid;
+                else hi = mid;
+            }
+            const int local = p - s_poff[lo];
+            const int r = s_off[lo] + local;
+            const int src = local < s_off[lo + 1] - s_off[lo] ? a.perm[r] : -1;
+            const bool ok = (uint64_t)(int64_t)src < (uint64_t)a.T;
+            s_src[threadIdx.x] = ok ? src : -1;
+        }
+        __syncthreads();
+        for (int c0 = 0; c0 < dpad; c0 += SPAN) {
+            const int ncol = min(SPAN, dpad - c0);
+            // rows wid, wid + 4, ... : every load of the wave first, then the LDS stores
+            constexpr int CPL = SPAN / 8 / kWave;   // 16-byte chunks per lane and row
+            uint4 v[4][CPL];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int src = s_src[wid + 4 * q];
+#pragma unroll
+                for (int i = 0; i < CPL; ++i) {
+                    const int c = lane + kWave * i;
+                    const int64_t cg = c0 / 8 + c;   // chunk of the row
+                    v[q][i] = make_uint4(0u, 0u, 0u, 0u);
+                    if (c < ncol / 8 && src >= 0 && cg < d16) v[q][i] = x4[(int64_t)src * d16 + cg];
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int i = 0; i < CPL; ++i) {
+                    const int c = lane + kWave * i;
+                    if (c < ncol / 8) *reinterpret_cast<uint4*>(&buf[(wid + 4 * q) * LROW + 8 * c]) = v[q][i];
+                }
+            __syncthreads();
+            const int row = lane >> 2, piece = lane & 3;
+            for (int t = wid; t < ncol / 32; t += 4) {
+                const uint4 v = *reinterpret_cast<const uint4*>(&buf[row * LROW + 32 * t + 8 * piece]);
+                t4[((int64_t)pb * KT + c0 / 32 + t) * 64 + row * 4 + piece] = v;
+            }
+            __syncthreads();
+        }
+    }
+    const int64_t S = s_off[E];
+    const int64_t nthreads = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t r = S + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < a.max_rows; r += nthreads)
+        a.perm[r] = -1;
+}
+
+hipError_t launch_gather_tiled(const DispatchArgs& a, uint16_t* x_pt, int d, hipStream_t st) {
+    if (a.E > 1024) return hipErrorInvalidValue;
+    int64_t blocks = h_tiled_rows(a.max_rows, a.E) / 16;   // one workgroup per 16-row block
+    if (blocks > 65536) blocks = 65536;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(gather_tiled_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a, x_pt, d);
+    return hipGetLastError();
+}
+
+// x_perm[slot[t, j]] = x[t] for every kept slot, one wave per token (the
+// backward's own copy of the rows when the caller passes no x_perm).
+__global__ __launch_bounds__(256) void gather_slots_kernel(int64_t T, int k, int64_t max_rows, int64_t row_bytes,
+                                                           const void* __restrict__ x,
+                                                           const int32_t* __restrict__ slot,
+                                                           void* __restrict__ x_perm) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t n16 = row_bytes / 16;
+    const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x / kWave);
+    for (int64_t t = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave; t < T; t += nwaves) {
+        const int my = lane < k ? slot[t * k + lane] : -1;
+        const uint64_t keep = __ballot((uint64_t)(int64_t)my < (uint64_t)max_rows);
+        const uint4* s4 = reinterpret_cast<const uint4*>(static_cast<const char*>(x) + t * row_bytes);
+        for (uint64_t m = keep; m != 0; m &= m - 1) {
+            const int j = __ffsll((unsigned long long)m) - 1;
+            const int64_t row = __shfl(my, j, kWave);
+            uint4* d4 = reinterpret_cast<uint4*>(static_cast<char*>(x_perm) + row * row_bytes);
+            for (int64_t c = lane; c < n16; c += kWave) d4[c] = s4[c];
+        }
+    }
+}
+
+hipError_t launch_gather_slots(int64_t T, int k, int64_t max_rows, int64_t row_bytes, const void* x,
+                               const int32_t* slot, void* x_perm, hipStream_t st) {
+    int64_t blocks = (T + 3) / 4;
+    if (blocks > 65536) blocks = 65536;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(gather_slots_kernel, dim3((unsigned)blocks), dim3(256), 0, st, T, k, max_rows, row_bytes, x,
+                       slot, x_perm);
+    return hipGetLastError();
 }
 
 hipError_t launch_hist(const DispatchArgs& a, hipStream_t st) {

@@ -166,24 +166,6 @@ __device__ __forceinline__ void store4(const GemmArgs& g, int64_t row, int64_t p
     }
 }
 
-// s_poff[e] = sum over e' < e of the expert's rows rounded up to 16 (from
-// s_off in LDS, visible to every thread); same scan as build_mtile_prefix.
-__device__ __forceinline__ void build_padded_offsets(const int* s_off, int E, int* s_poff, int* tmp) {
-    const int tid = threadIdx.x;
-    const int per = (E + blockDim.x - 1) / blockDim.x;
-    const int lo = tid * per;
-    int local = 0;
-    for (int e = lo; e < lo + per && e < E; ++e) local += (s_off[e + 1] - s_off[e] + 15) & ~15;
-    const int incl = block_inclusive_scan(local, tmp);
-    int run = incl - local;
-    for (int e = lo; e < lo + per && e < E; ++e) {
-        s_poff[e] = run;
-        run += (s_off[e + 1] - s_off[e] + 15) & ~15;
-    }
-    if (tid == blockDim.x - 1) s_poff[E] = incl;
-    __syncthreads();
-}
-
 // Per-lane global -> LDS load geometry and the work item it streams from.
 template <class C>
 struct Item {
@@ -582,7 +564,7 @@ __device__ __forceinline__ void epilogue32(const GemmArgs& g, const Item<C>& it,
 // Small tiles: every wave reads and multiplies each step; one s_waitcnt
 // vmcnt + s_barrier per step publishes the oldest stage and frees the one
 // consumed before it.
-template <class C, int EPI>
+template <class C, int EPI, bool AT = kATiled<EPI>>
 __global__ __launch_bounds__(C::NT) void ffn_gemm_bf16_kernel(GemmArgs g) {
     static_assert(C::MF == 16, "small tiles use the 16x16x32 form");
     __shared__ __attribute__((aligned(1024))) uint16_t sa[NSTAGE][C::BM * BK];
@@ -605,7 +587,7 @@ __global__ __launch_bounds__(C::NT) void ffn_gemm_bf16_kernel(GemmArgs g) {
     build_padded_offsets(s_off, E, s_poff, scan_tmp);
     const ItemRange range = xcd_item_range((int64_t)total_mt * ntn);
     if (range.first >= range.end) return;
-    const Loader<C, kATiled<EPI>> ld(g, s_off, mt_pre, s_poff, ntn, wid, lane);
+    const Loader<C, AT> ld(g, s_off, mt_pre, s_poff, ntn, wid, lane);
 
     constexpr int PER = C::A_DMA + C::B_DMA;   // vector-memory ops per stage per lane
     int64_t item = range.first;
@@ -812,9 +794,9 @@ static int persistent_blocks(KernelFn kernel, int threads) {
     return blocks < kXcds ? kXcds : blocks;
 }
 
-template <class C, int EPI>
+template <class C, int EPI, bool AT>
 static int small_blocks() {
-    static const int blocks = persistent_blocks(ffn_gemm_bf16_kernel<C, EPI>, C::NT);
+    static const int blocks = persistent_blocks(ffn_gemm_bf16_kernel<C, EPI, AT>, C::NT);
     return blocks;
 }
 
@@ -848,17 +830,19 @@ static bool try_pipe(const GemmArgs& g, int64_t max_rows, hipStream_t st, hipErr
     return true;
 }
 
-template <int EPI>
+template <int EPI, bool AT = kATiled<EPI>>
 static hipError_t launch_epi(const GemmArgs& g, int64_t max_rows, hipStream_t st) {
     hipError_t err = hipSuccess;
-    if (try_pipe<TilePipe, 4, 1024, TilePipe::NW >= 8 ? 2 : 1, EPI>(g, max_rows, st, &err)) return err;
-    hipLaunchKernelGGL((ffn_gemm_bf16_kernel<TileSmall, EPI>), dim3(small_blocks<TileSmall, EPI>()),
+    if (try_pipe<TilePipe, 4, 1024, TilePipe::NW >= 8 ? 2 : 1, EPI, AT>(g, max_rows, st, &err)) return err;
+    hipLaunchKernelGGL((ffn_gemm_bf16_kernel<TileSmall, EPI, AT>), dim3(small_blocks<TileSmall, EPI, AT>()),
                        dim3(TileSmall::NT), 0, st, g);
     return hipGetLastError();
 }
 
-hipError_t launch_ffn_gemm_bf16(const GemmArgs& g, int epi, int64_t max_rows, hipStream_t st) {
-    return epi == EPI_GELU_H ? launch_epi<EPI_GELU_H>(g, max_rows, st) : launch_epi<EPI_STORE_F32>(g, max_rows, st);
+hipError_t launch_ffn_gemm_bf16(const GemmArgs& g, int epi, int64_t max_rows, hipStream_t st, bool a_tiled) {
+    if (epi == EPI_GELU_H)
+        return a_tiled ? launch_epi<EPI_GELU_H, true>(g, max_rows, st) : launch_epi<EPI_GELU_H>(g, max_rows, st);
+    return launch_epi<EPI_STORE_F32>(g, max_rows, st);
 }
 
 bool launch_ffn_gemm_bf16_pipe(const GemmArgs& g, int epi, bool b_kc, int64_t max_rows, hipStream_t st,

@@ -43,6 +43,24 @@ __device__ __forceinline__ int build_mtile_prefix(const int32_t* __restrict__ of
     return mt_pre[E];
 }
 
+// s_poff[e] = sum over e' < e of the expert's rows rounded up to 16 (from
+// s_off in LDS, visible to every thread); same scan as build_mtile_prefix.
+__device__ __forceinline__ void build_padded_offsets(const int* s_off, int E, int* s_poff, int* tmp) {
+    const int tid = threadIdx.x;
+    const int per = (E + blockDim.x - 1) / blockDim.x;
+    const int lo = tid * per;
+    int local = 0;
+    for (int e = lo; e < lo + per && e < E; ++e) local += (s_off[e + 1] - s_off[e] + 15) & ~15;
+    const int incl = block_inclusive_scan(local, tmp);
+    int run = incl - local;
+    for (int e = lo; e < lo + per && e < E; ++e) {
+        s_poff[e] = run;
+        run += (s_off[e + 1] - s_off[e] + 15) & ~15;
+    }
+    if (tid == blockDim.x - 1) s_poff[E] = incl;
+    __syncthreads();
+}
+
 struct WorkItem {
     int e, nt, mt;
 };

@@ -100,7 +100,7 @@ static int validate(const moe_shape* s, Geo* g) {
 }
 
 struct WsLayout {
-    size_t gate, blkhist, offsets, idx, w, perm, slot, xperm, h, out, total;
+    size_t gate, blkhist, offsets, idx, w, perm, slot, xperm, xpt, h, out, total;
 };
 
 static size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
@@ -121,6 +121,9 @@ static WsLayout ws_layout(const Geo& g) {
     L.perm = take(sizeof(int32_t) * (size_t)g.max_rows);
     L.slot = take(sizeof(int32_t) * (size_t)(g.T * g.k));
     L.xperm = take((size_t)g.esz * (size_t)g.max_rows * g.d);
+    // bf16: x_perm again in the h tile layout, GEMM1's operand in moe_layer_forward
+    L.xpt = take(g.esz == 2 ? (size_t)g.esz * (size_t)h_tiled_rows(g.max_rows, g.E) * (size_t)((g.d + 31) / 32 * 32)
+                            : 0);
     // bf16: h in 16 x 32 tiles over 16-row-padded expert segments (ffn_bf16.hip)
     L.h = take(g.esz == 2 ? (size_t)g.esz * (size_t)h_tiled_rows(g.max_rows, g.E) * (size_t)((g.dff + 31) / 32 * 32)
                           : (size_t)g.esz * (size_t)g.max_rows * g.dff);
@@ -189,8 +192,8 @@ static DispatchArgs dispatch_args(const Geo& g, const moe_shape* s) {
     return a;
 }
 
-static hipError_t launch_gemm(const Geo& g, const GemmArgs& ga, int epi, hipStream_t st) {
-    return g.esz == 2 ? launch_ffn_gemm_bf16(ga, epi, g.max_rows, st) : launch_ffn_gemm_f32(ga, epi, st);
+static hipError_t launch_gemm(const Geo& g, const GemmArgs& ga, int epi, hipStream_t st, bool a_tiled = false) {
+    return g.esz == 2 ? launch_ffn_gemm_bf16(ga, epi, g.max_rows, st, a_tiled) : launch_ffn_gemm_f32(ga, epi, st);
 }
 
 }  // namespace moe
@@ -228,6 +231,7 @@ int64_t moe_workspace_offset(const moe_shape* s, int which) {
         case MOE_WS_XPERM: return (int64_t)L.xperm;
         case MOE_WS_H: return (int64_t)L.h;
         case MOE_WS_OUT: return (int64_t)L.out;
+        case MOE_WS_XPT: return (int64_t)L.xpt;
         default: fail(MOE_ERR_SHAPE, "unknown workspace region %d", which); return -1;
     }
 }
@@ -431,7 +435,7 @@ int moe_aux_loss_ex(const moe_shape* s, int mode, const int32_t* load, float* au
 }
 
 struct BwLayout {
-    size_t g, h, hgrad, da, dx_perm, dw, dl, dxg, dwg_part, total;
+    size_t g, h, hgrad, da, dx_perm, dw, dl, dxg, dwg_part, xperm, total;
     int gate_chunks, gate_chunk;
 };
 
@@ -456,6 +460,7 @@ static BwLayout bw_layout(const Geo& g) {
     L.gate_chunks = (int)std::min<int64_t>(64, (g.T + 511) / 512);
     L.gate_chunk = (int)((g.T + L.gate_chunks - 1) / L.gate_chunks);
     L.dwg_part = take(4 * (size_t)L.gate_chunks * g.d * g.E);
+    L.xperm = take((size_t)g.esz * R * g.d);   // the rows of x when the caller passes no x_perm
     L.total = p;
     return L;
 }
@@ -483,7 +488,7 @@ int moe_layer_backward(const moe_shape* s, const void* x, const float* Wg, const
     MOE_REQUIRE(topk_w);
     MOE_REQUIRE(slot);
     MOE_REQUIRE(offsets);
-    MOE_REQUIRE(x_perm);
+    MOE_OPTIONAL(x_perm);
     MOE_REQUIRE(out_perm);
     MOE_REQUIRE(dx);
     MOE_REQUIRE(dWg);
@@ -506,7 +511,8 @@ int moe_layer_backward(const moe_shape* s, const void* x, const float* Wg, const
     b.tau = s->temperature;
     b.x = x; b.Wg = Wg; b.W1 = W1; b.b1 = b1; b.W2 = W2;
     b.dy = dy; b.topk_idx = topk_idx; b.topk_w = topk_w; b.slot = slot; b.offsets = offsets;
-    b.x_perm = x_perm; b.out_perm = out_perm;
+    b.x_perm = x_perm != nullptr ? x_perm : at<void>(ws, L.xperm);
+    b.out_perm = out_perm;
     b.dx = dx; b.dWg = dWg; b.dbg = dbg; b.dW1 = dW1; b.db1 = db1; b.dW2 = dW2; b.db2 = db2;
     b.g = at<float>(ws, L.g);
     b.h = at<void>(ws, L.h);
@@ -520,6 +526,9 @@ int moe_layer_backward(const moe_shape* s, const void* x, const float* Wg, const
     b.gate_chunks = L.gate_chunks;
     b.gate_chunk = L.gate_chunk;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (x_perm == nullptr)
+        MOE_HIP(launch_gather_slots(g.T, (int)g.k, g.max_rows, g.d * g.esz, x, slot, at<void>(ws, L.xperm), st),
+                "backward gather launch");
     MOE_HIP(launch_layer_backward(b, s->dtype, st), "backward kernel launch");
     return MOE_OK;
 }
@@ -617,13 +626,17 @@ int moe_layer_forward(const moe_shape* s, const void* x, const float* Wg, const 
     stage_event(2, 0, st);
     MOE_HIP(launch_scatter(da, st), "scatter kernel launch");
     stage_event(2, 1, st);
+    // bf16: x_perm row-major (the layout moe_layer_backward reads) plus the
+    // tile layout GEMM1 loads in contiguous KiBs
+    const bool tiled = g.esz == 2;
     stage_event(3, 0, st);
-    MOE_HIP(launch_gather(da, st), "gather kernel launch");
+    if (tiled) MOE_HIP(launch_gather_tiled(da, at<uint16_t>(ws, L.xpt), (int)g.d, st), "gather kernel launch");
+    else MOE_HIP(launch_gather(da, st), "gather kernel launch");
     stage_event(3, 1, st);
 
     // 3. grouped FFN over the expert-contiguous rows
     GemmArgs g1{};
-    g1.A = da.x_perm;
+    g1.A = tiled ? at<void>(ws, L.xpt) : da.x_perm;
     g1.B = W1;
     g1.bias = b1;
     g1.offsets = da.offsets;
@@ -632,7 +645,7 @@ int moe_layer_forward(const moe_shape* s, const void* x, const float* Wg, const 
     g1.N = (int)g.dff;
     g1.out = at<void>(ws, L.h);
     stage_event(4, 0, st);
-    MOE_HIP(launch_gemm(g, g1, EPI_GELU_H, st), "ffn1 kernel launch");
+    MOE_HIP(launch_gemm(g, g1, EPI_GELU_H, st, tiled), "ffn1 kernel launch");
     stage_event(4, 1, st);
     GemmArgs g2 = g1;
     g2.A = g1.out;

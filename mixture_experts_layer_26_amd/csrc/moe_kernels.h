@@ -54,6 +54,13 @@ struct DispatchArgs {
 };
 int dispatch_block_tokens(int64_t T, int E, int k);
 hipError_t launch_hist(const DispatchArgs& a, hipStream_t st);
+// the fused bf16 forward's copy: x_pt = the rows of x_perm in the h tile
+// layout over h_tiled_rows(max_rows, E) rows of 32 ceil(d/32) columns
+// (padding rows and columns zero); perm is padded with -1 as by launch_gather
+hipError_t launch_gather_tiled(const DispatchArgs& a, uint16_t* x_pt, int d, hipStream_t st);
+// x_perm[slot[t, j]] = x[t] for the kept slots (row-major, row_bytes per row)
+hipError_t launch_gather_slots(int64_t T, int k, int64_t max_rows, int64_t row_bytes, const void* x,
+                               const int32_t* slot, void* x_perm, hipStream_t st);
 hipError_t launch_scatter(const DispatchArgs& a, hipStream_t st);
 hipError_t launch_gather(const DispatchArgs& a, hipStream_t st);
 
@@ -79,7 +86,8 @@ struct GemmArgs {
 };
 // rows of the h tile layout for max_rows packed rows over E experts
 inline int64_t h_tiled_rows(int64_t max_rows, int64_t E) { return ((max_rows + 15 * E + 15) / 16) * 16; }
-hipError_t launch_ffn_gemm_bf16(const GemmArgs& g, int epi, int64_t max_rows, hipStream_t st);
+// a_tiled (EPI_GELU_H): A is x_perm in the h tile layout (gather_tiled_kernel)
+hipError_t launch_ffn_gemm_bf16(const GemmArgs& g, int epi, int64_t max_rows, hipStream_t st, bool a_tiled = false);
 // The pipelined 256 x 256 bf16 kernel with explicit operand layouts (the
 // backward's expert GEMMs): A row-major (not the h tile layout); B as [E, K, N]
 // or, b_kc, [E, N, K] (then K must be a multiple of 32).  Returns false and

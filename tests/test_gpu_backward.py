@@ -54,7 +54,9 @@ def forward_backward(moe, cfg, inp, dy):
 
     slot = region(moe.MOE_WS_SLOT, i32, (T, k))
     offsets = region(moe.MOE_WS_OFFSETS, i32, (E + 1,))
-    xperm = region(moe.MOE_WS_XPERM, torch.int16 if esz == 2 else f32, (R, d))
+    # a bf16 forward keeps x_perm only in the tile layout: the backward then
+    # copies the rows of x itself (x_perm = None)
+    xperm = region(moe.MOE_WS_XPERM, f32, (R, d)) if esz == 4 else None
     out = region(moe.MOE_WS_OUT, f32, (R, d))
     bws = moe.backward_workspace(s)
     g = dict(dx=H.empty((T, d), f32), dWg=H.empty((d, E), f32), dbg=H.empty(E, f32), dW1=H.empty((E, d, F), f32),
