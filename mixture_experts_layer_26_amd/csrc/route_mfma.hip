@@ -33,6 +33,12 @@ __device__ __forceinline__ bool beats(float av, int ai, float bv, int bi) {
     return av > bv || (av == bv && ai < bi);
 }
 
+// 128-byte tile rows (two K-steps): logical 16-byte chunk c of row r sits at
+// physical chunk c ^ ((r >> 1) & 7), so the 16 rows one 16-lane group reads
+// (one chunk each) cover all 16 chunk positions of a 256-byte bank window
+__device__ __forceinline__ int w128_swz(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int w128_at(int r, int c) { return r * 64 + 8 * (c ^ w128_swz(r)); }
+
 }  // namespace
 
 __global__ __launch_bounds__(256) void split_gate_kernel(const float* __restrict__ Wg, int d, int E, int EP2,
@@ -180,22 +186,31 @@ __global__ __launch_bounds__(64 * NW) void route_mfma_kernel(RouteArgs a, const 
     const int nk = (d + BKG - 1) / BKG;          // K-steps
     const int nst = (nk + KS - 1) / KS;          // stages
 
-    // load geometry of this lane: wave load j = wid * PER + i covers K-step
-    // j / INSTR1 of the stage, tile rows 16 (j % INSTR1) .. +15; lane -> row
-    // 16 (j % INSTR1) + lane / 4, physical slot lane % 4, logical chunk
-    // c = slot ^ swz(row), i.e. K offset 8 c of that K-step
+    // load geometry of this lane.  KS = 1: wave load j = wid * PER + i
+    // covers tile rows 16 j .. +15 of the K-step; lane -> row 16 j + lane / 4,
+    // physical slot lane % 4, logical chunk c = slot ^ swz(row), i.e. K
+    // offset 8 c.  KS = 2: rows are 128 bytes (both K-steps of the stage, a
+    // global -> LDS load of 128-byte pieces moves twice the bytes per cycle of
+    // one of 64-byte pieces); load j covers rows 8 j .. +7, lane -> row
+    // 8 j + lane / 8, physical chunk lane % 8, logical chunk c = chunk ^
+    // w128_swz(row), K offset 8 c of the stage.
+    static_assert(KS == 1 || KS == 2, "one or two K-steps per stage");
+    constexpr bool W128 = KS == 2;
     const int64_t valid = T - t0 < BM ? T - t0 : BM;
     const i32x4_t rsx = make_rsrc(static_cast<const uint16_t*>(a.x) + t0 * d, (uint32_t)(valid * d * 2));
     const i32x4_t rsw = make_rsrc(W3, (uint32_t)(3u * EP2 * (uint32_t)d * 2u));
     int base[PER], c8[PER];
+    bool isx[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int j = wid * PER + i;
-        const int r = 16 * (j % INSTR1) + (lane >> 2);
-        const int c = (lane & 3) ^ k64_swz(r);
+        const int r = W128 ? 8 * j + (lane >> 3) : 16 * (j % INSTR1) + (lane >> 2);
+        const int c = W128 ? (lane & 7) ^ w128_swz(r) : (lane & 3) ^ k64_swz(r);
         const int src_row = r < BM ? r : r - BM;    // token row of the block, or weight row s * EP2 + e
-        base[i] = (src_row * d + 8 * c + BKG * (j / INSTR1)) * 2;
-        c8[i] = 8 * c + BKG * (j / INSTR1);
+        const int kofs = W128 ? 8 * c : 8 * c + BKG * (j / INSTR1);
+        base[i] = (src_row * d + kofs) * 2;
+        c8[i] = kofs;
+        isx[i] = r < BM;
     }
     auto issue = [&](int st, int slot) {   // st >= nst: every load out of range
         const int k0 = st * KS * BKG;
@@ -204,7 +219,7 @@ __global__ __launch_bounds__(64 * NW) void route_mfma_kernel(RouteArgs a, const 
             const int j = wid * PER + i;
             const bool ok = j < INSTR && st < nst && k0 + c8[i] < d;
             const int off = ok ? base[i] + 2 * k0 : kOutOfRange;
-            dma16(16 * (j % INSTR1) < BM ? rsx : rsw, &sm.ring[slot][j * 512], off);
+            dma16(isx[i] ? rsx : rsw, &sm.ring[slot][j * 512], off);
         }
     };
 
@@ -230,13 +245,16 @@ __global__ __launch_bounds__(64 * NW) void route_mfma_kernel(RouteArgs a, const 
             const uint16_t* sq = sp + q * INSTR1 * 512;
 #pragma unroll
             for (int mb = 0; mb < MBW; ++mb)
-                xf[q][mb] = *reinterpret_cast<const bf16x8_t*>(&sq[k64_slot((wm * MBW + mb) * 16 + i16, g16) * 8]);
+                xf[q][mb] = *reinterpret_cast<const bf16x8_t*>(
+                    W128 ? &sp[w128_at((wm * MBW + mb) * 16 + i16, 4 * q + g16)]
+                         : &sq[k64_slot((wm * MBW + mb) * 16 + i16, g16) * 8]);
 #pragma unroll
             for (int s = 0; s < 3; ++s)
 #pragma unroll
                 for (int nb = 0; nb < NBW; ++nb)
                     wf[q][s][nb] = *reinterpret_cast<const bf16x8_t*>(
-                        &sq[k64_slot(BM + s * EP2 + (wn * NBW + nb) * 16 + i16, g16) * 8]);
+                        W128 ? &sp[w128_at(BM + s * EP2 + (wn * NBW + nb) * 16 + i16, 4 * q + g16)]
+                             : &sq[k64_slot(BM + s * EP2 + (wn * NBW + nb) * 16 + i16, g16) * 8]);
         }
 #pragma unroll
         for (int q = 0; q < KS; ++q) {
