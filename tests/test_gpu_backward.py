@@ -33,7 +33,7 @@ def moe():
     return m
 
 
-def forward_backward(moe, cfg, inp, dy):
+def forward_backward(moe, cfg, inp, dy, xperm_from_dispatch=False):
     import torch
     dv = H.dev_inputs(inp)
     s = H.make_shape(moe, cfg)
@@ -55,8 +55,13 @@ def forward_backward(moe, cfg, inp, dy):
     slot = region(moe.MOE_WS_SLOT, i32, (T, k))
     offsets = region(moe.MOE_WS_OFFSETS, i32, (E + 1,))
     # a bf16 forward keeps x_perm only in the tile layout: the backward then
-    # copies the rows of x itself (x_perm = None)
+    # copies the rows of x itself (x_perm = None); or x_perm from
+    # moe_dispatch on the forward's routing (its own workspace)
     xperm = region(moe.MOE_WS_XPERM, f32, (R, d)) if esz == 4 else None
+    if xperm_from_dispatch:
+        xperm = H.empty((R, d), torch.int16 if esz == 2 else f32)
+        moe.moe_dispatch(s, dv["x"], idx, H.empty(E, i32), H.empty(E, i32), H.empty(E + 1, i32), H.empty(R, i32),
+                         H.empty((T, k), i32), xperm, moe.workspace(s))
     out = region(moe.MOE_WS_OUT, f32, (R, d))
     bws = moe.backward_workspace(s)
     g = dict(dx=H.empty((T, d), f32), dWg=H.empty((d, E), f32), dbg=H.empty(E, f32), dW1=H.empty((E, d, F), f32),
@@ -83,6 +88,21 @@ def test_backward_small(moe, orc, name):
     tol = TOL[cfg.dtype]
     for n in ("dx", "dWg", "dbg", "dW1", "db1", "dW2", "db2"):
         H.assert_close_norm(got[n], ref[n], tol, f"{name} {n}")
+
+
+@pytest.mark.parametrize("name", ["ragged_bf16", "medium_bf16", "ragged_fp32"])
+def test_backward_xperm_given_or_copied(moe, name):
+    """x_perm passed in (moe_dispatch's row-major rows) and x_perm = None
+    (the backward copies the kept rows of x by slot) give the same gradients,
+    bit for bit."""
+    cfg = get(name)
+    inp = make_inputs(cfg)
+    dy = dy_of(cfg)
+    a, La, _, _ = forward_backward(moe, cfg, inp, dy)
+    b, Lb, _, _ = forward_backward(moe, cfg, inp, dy, xperm_from_dispatch=True)
+    assert np.array_equal(La, Lb)
+    for n in a:
+        assert np.array_equal(a[n], b[n]), f"{name} {n}: x_perm given vs copied"
 
 
 @pytest.mark.parametrize("name", ["skewed_e64", "skewed_e64_literal", "dense_soft_e16"])
