@@ -144,10 +144,11 @@ const char* moe_version(void);
  *    accumulated in fp32 ([PithTrain] 4.1: linear gate, top-k, softmax over
  *    the selected values; [PyTorchMoE] 3.2: the gate may carry a bias;
  *    [EP] 5.5: routing kept in fp32).  Writes topk_idx and topk_w; also the
- *    logits when `logits` is not NULL.  For bf16 x with E <= 256 the gate
- *    runs on the matrix cores with Wg split exactly into three bf16 parts
- *    (kept in the workspace), which gives fp32-accurate products; otherwise
- *    on the vector ALUs in fp32.  ws: at least moe_workspace_size bytes. */
+ *    logits when `logits` is not NULL.  For bf16 x with E <= 256 and
+ *    k <= 16 the gate runs on the matrix cores with Wg split exactly into
+ *    three bf16 parts (kept in the workspace), which gives fp32-accurate
+ *    products; otherwise on the vector ALUs in fp32.  Either way the same
+ *    selection rule and weights.  ws: at least moe_workspace_size bytes. */
 int moe_route(const moe_shape* s, const void* x, const float* Wg, const float* bg,
               float* logits /* NULL ok */, int32_t* topk_idx, float* topk_w,
               void* ws, size_t ws_bytes, void* stream);
