@@ -73,6 +73,35 @@ def test_workspace_layout(moe):
     assert moe.moe_workspace_offset(s, 99) == -1
 
 
+def _header_enum(prefix):
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    return {m.group(1): int(m.group(2)) for m in re.finditer(r"(%s\w+)\s*=\s*(\d+)" % prefix, src)}
+
+
+def test_workspace_regions_follow_the_header(moe):
+    """The MOE_WS_* values of the binding are the header's; every region of a
+    bf16 and an fp32 layer is 256-byte aligned, the regions do not overlap and
+    each holds its documented size (bf16: x_perm also in the tile layout over
+    h_tiled_rows = 16 ceil((max_rows + 15 E) / 16) rows of 32 ceil(d / 32)
+    columns)."""
+    enum = _header_enum("MOE_WS_")
+    assert enum and all(getattr(moe, k) == v for k, v in enum.items()), enum
+    for dtype, esz in ((moe.MOE_BF16, 2), (moe.MOE_F32, 4)):
+        T, d, E, k, F = 3000, 200, 12, 3, 328
+        s = moe.shape(T, d, E, k, F, 1.0, 1.0, 0.01, dtype)
+        R = moe.moe_max_rows(s)
+        ht = (R + 15 * E + 15) // 16 * 16
+        size = {moe.MOE_WS_PERM: 4 * R, moe.MOE_WS_SLOT: 4 * T * k, moe.MOE_WS_OFFSETS: 4 * (E + 1),
+                moe.MOE_WS_XPERM: esz * R * d, moe.MOE_WS_OUT: 4 * R * d,
+                moe.MOE_WS_H: 2 * ht * ((F + 31) // 32 * 32) if esz == 2 else 4 * R * F,
+                moe.MOE_WS_XPT: 2 * ht * ((d + 31) // 32 * 32) if esz == 2 else 0}
+        spans = sorted((moe.moe_workspace_offset(s, w), size[w]) for w in enum.values())
+        assert all(o % 256 == 0 for o, _ in spans)
+        for (o1, n1), (o2, _) in zip(spans, spans[1:]):
+            assert o1 + n1 <= o2
+        assert spans[-1][0] + spans[-1][1] <= moe.moe_workspace_size(s)
+
+
 BAD_SHAPES = [
     dict(T=0), dict(E=0), dict(E=1025), dict(k=0), dict(k=9, E=8), dict(k=33, E=64),
     dict(d=0), dict(d=12), dict(d_ff=20), dict(temperature=0.0), dict(temperature=float("inf")),
