@@ -17,7 +17,10 @@
 //             block 0 also writes routed, counts, offsets and the balance
 //             loss ([EP] section 2.3);
 //   gather  : x_perm[row] = x[perm[row]] with 16-byte vector copies, one
-//             wave per row; pads perm with -1 past the used rows.
+//             wave per row; pads perm with -1 past the used rows (the fused
+//             bf16 forward uses gather_tiled_kernel instead: the same rows
+//             in the grouped GEMM's tile layout).
+// gather_slots_kernel is the backward's copy of the rows, by slot.
 #include "ffn_sched.h"
 #include "moe_common.h"
 #include "moe_kernels.h"
@@ -159,8 +162,8 @@ __global__ __launch_bounds__(256) void gather_kernel(DispatchArgs a) {
 }
 
 // The fused bf16 forward's copy: x_perm[row] = x[perm[row]] in the grouped
-// GEMM's 16-row x 32-column tile layout over expert segments
-// padded to 16 rows (padded row p, column c at ((p / 16) KT + c / 32) 512 +
+// GEMM's 16-row x 32-column tile layout over expert segments padded to 16
+// rows (padded row p, column c at ((p / 16) KT + c / 32) 512 +
 // (p % 16) 32 + c % 32, KT = ceil(d / 32)).  In that layout one K-step of 16
 // rows of GEMM1's activation operand is one contiguous KiB: a global -> LDS
 // load of 64-byte row pieces moves half as many bytes per cycle as one of

@@ -33,6 +33,11 @@
 //     c % 32 with KT = ceil(d_ff / 32); GEMM1 writes zeros into columns
 //     [d_ff, 32 KT), so GEMM2's K tail multiplies zeros.  Padding rows are
 //     never written; each feeds only its own output row, which is not stored.
+//   * in the fused forward GEMM1's activations come in the same tile layout
+//     (x_perm over ceil(d / 32) column tiles, written by the dispatch's tiled
+//     copy): a global -> LDS load of 64-byte row pieces moves half the bytes
+//     per cycle of one of contiguous KiBs.  moe_grouped_ffn's GEMM1 reads the
+//     caller's row-major x_perm.
 //
 // Two schedules:
 //   * large problems: 256 x 256 tiles on eight waves (two per SIMD), each a
