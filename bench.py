@@ -94,10 +94,11 @@ def parse():
 def dispatch_block_tokens(T, E, k):
     """Tokens per histogram/scatter block, the library's rule: 1024 (512 above
     256 experts, 256 above 512), halved while a block holds more than 2048
-    slots and the block count stays <= 256 (only the reported bytes of the
-    two dispatch launches depend on it)."""
+    slots or there are fewer than 16 blocks, as long as the block count stays
+    <= 256 (only the reported bytes of the two dispatch launches depend on
+    it)."""
     bt = 1024 if E <= 256 else 512 if E <= 512 else 256
-    while bt > 64 and bt * k > 2048 and (T + bt // 2 - 1) // (bt // 2) <= 256:
+    while bt > 64 and (bt * k > 2048 or (T + bt - 1) // bt < 16) and (T + bt // 2 - 1) // (bt // 2) <= 256:
         bt //= 2
     return bt
 

@@ -30,11 +30,13 @@ namespace moe {
 int dispatch_block_tokens(int64_t T, int E, int k) {
     // bitmask bytes E * BT / 8 kept <= 32 KiB
     int bt = E <= 256 ? 1024 : E <= 512 ? 512 : 256;
-    // aim at <= 2048 slots per block: with k = 8 or 16 choices per token a
-    // 1024-token block leaves most CUs idle (8 blocks for 8192 tokens) while
-    // each thread walks 8-16 slots.  Every scatter block reads the whole
-    // [nblk x E] histogram, so blocks are not split past 256 of them.
-    while (bt > 64 && bt * k > 2048 && (T + bt / 2 - 1) / (bt / 2) <= 256) bt >>= 1;
+    // aim at <= 2048 slots per block and at least 16 blocks: with k = 8 or 16
+    // choices per token a 1024-token block leaves most CUs idle (8 blocks for
+    // 8192 tokens) while each thread walks 8-16 slots, and 4 or 8 blocks of
+    // two choices per token left the scatter 2 us slower (4096 and 8192
+    // tokens).  Every scatter block reads the whole [nblk x E] histogram, so
+    // blocks are not split past 256 of them.
+    while (bt > 64 && (bt * k > 2048 || (T + bt - 1) / bt < 16) && (T + bt / 2 - 1) / (bt / 2) <= 256) bt >>= 1;
     return bt;
 }
 
