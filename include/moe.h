@@ -3,7 +3,7 @@
  *
  * One GPU's share of a Mixture-of-Experts layer forward:
  *   gate GEMM -> top-k + softmax -> capacity-limited dispatch into
- *   expert-contiguous rows -> grouped expert FFN (Linear d->d_ff, exact GELU,
+ *   expert-contiguous rows -> grouped expert FFN (Linear d->d_ff, erf GELU,
  *   Linear d_ff->d) -> routing-weighted combine -> per-expert counts and
  *   balance loss.
  *
@@ -56,7 +56,10 @@
  * Precision: the gate accumulates in fp32; the expert GEMMs take bf16 (or
  *   fp32) operands with fp32 accumulation; bias, GELU, routing weights and
  *   the combine are fp32; h is stored in the layer dtype (bf16 rounded to
- *   nearest even) ([EP] 5.5: route in fp32, experts in bf16).
+ *   nearest even) ([EP] 5.5: route in fp32, experts in bf16).  GELU is the
+ *   erf form u Phi(u); fp32 layers evaluate erf with the device library's
+ *   erff, bf16 layers with Abramowitz & Stegun eq. 7.1.26 (absolute error
+ *   <= 1.5e-7 on erf, far below the bf16 rounding of h).
  * Errors: every entry point validates its arguments on the host first.  On a
  *   validation failure it returns a non-zero moe_status, launches nothing and
  *   writes nothing; moe_last_error() then holds a message for the calling
@@ -117,7 +120,8 @@ size_t moe_workspace_size(const moe_shape* s);
  * moe_layer_forward leaves there, for inspection after the call completes:
  * which = MOE_WS_PERM (int32 [max_rows]), MOE_WS_SLOT (int32 [T,k]),
  * MOE_WS_OFFSETS (int32 [E+1]), MOE_WS_XPERM (dtype [max_rows,d]; fp32
- * layers only -- a bf16 layer's forward keeps x_perm only as MOE_WS_XPT),
+ * layers only: -1 for a bf16 layer, whose forward keeps x_perm only as
+ * MOE_WS_XPT),
  * MOE_WS_XPT (bf16 layers: x_perm in the tile layout of MOE_WS_H below with
  * ceil(d/32) column tiles, the first GEMM's operand; padding rows and columns
  * d..32*ceil(d/32)-1 are zero),
@@ -174,8 +178,8 @@ int moe_dispatch(const moe_shape* s, const void* x, const int32_t* topk_idx,
 /* 3. Grouped expert FFN over the packed rows: for every row r of expert e
  *    (offsets[e] <= r < offsets[e+1]),
  *      out_perm[r] = GELU(x_perm[r] W1[e] + b1[e]) W2[e] + b2[e]
- *    with the exact erf GELU ([PithTrain] 4.1 expert = Linear, GELU, Linear;
- *    [PyTorchMoE] 3.2 Expert with biases).  offsets must be non-decreasing
+ *    with the erf GELU of the precision note above ([PithTrain] 4.1 expert =
+ *    Linear, GELU, Linear; [PyTorchMoE] 3.2 Expert with biases).  offsets must be non-decreasing
  *    with offsets[0] = 0 and offsets[E] <= max_rows.  Rows >= offsets[E] of
  *    out_perm are not written.  h lives in the workspace. */
 int moe_grouped_ffn(const moe_shape* s, const void* x_perm, const int32_t* offsets,
@@ -275,7 +279,7 @@ int moe_layer_forward(const moe_shape* s, const void* x, const float* Wg, const 
  * (selection, capacity, drops) fixed: they are piecewise constant.  The
  * layer is differentiated as autograd would differentiate [PithTrain]
  * section 4.1's layer: the combine y[t] += w[t,j] o[r], the expert FFN
- * o = GELU(x W1 + b1) W2 + b2 (exact erf GELU, derivative Phi(a) + a phi(a))
+ * o = GELU(x W1 + b1) W2 + b2 (erf GELU, derivative Phi(a) + a phi(a))
  * and the gate w = softmax(l_sel / temperature) with l = x Wg + bg; the
  * balance loss depends on integer counts only and has no gradient.  Experts
  * that received no row get zero weight and bias gradients ([EP] section
@@ -291,11 +295,17 @@ int moe_layer_forward(const moe_shape* s, const void* x, const float* Wg, const 
  * outputs.  dy [T,d] fp32.
  * Outputs (fp32, overwritten): dx [T,d], dWg [d,E], dbg [E], dW1
  * [E,d,d_ff], db1 [E,d_ff], dW2 [E,d_ff,d], db2 [E,d].
- * Arithmetic: fp32 on the vector ALUs; bf16 operands are widened exactly;
- * h is recomputed from x_perm, W1, b1 (rounded to the layer dtype, as the
- * forward stores it).  ws: moe_backward_workspace_size bytes (its own
- * workspace; the forward's may be read through x_perm / out_perm, so the
- * two must not overlap). */
+ * Arithmetic.  fp32 layers: every GEMM in fp32 on the vector ALUs.  bf16
+ * layers: the expert GEMMs run on bf16 matrix cores with fp32
+ * accumulation, so their operands are rounded to bf16 -- the expert-output
+ * gradient w[t,j] dy[t] and da = dh GELU'(a) (2^-9 relative each, like h);
+ * h is recomputed from x_perm, W1, b1 and rounded to bf16 as the forward
+ * stores it, GELU and GELU' use the forward's erf approximation; db1 and
+ * db2 are fp32 column sums of those bf16 values; the gate's GEMMs (dWg,
+ * the gate's part of dx) run in fp32 on the vector ALUs (bf16 x widened
+ * exactly).  ws: moe_backward_workspace_size bytes (its own workspace; the
+ * forward's may be read through x_perm / out_perm, so the two must not
+ * overlap). */
 size_t moe_backward_workspace_size(const moe_shape* s);
 int moe_layer_backward(const moe_shape* s, const void* x, const float* Wg, const void* W1, const float* b1,
                        const void* W2, const float* dy, const int32_t* topk_idx, const float* topk_w,

@@ -1,4 +1,4 @@
-// backward.hip -- backward of the MoE layer forward (gfx950, fp32 vector ALUs).
+// backward.hip -- backward of the MoE layer forward (gfx950).
 //
 // Gradients of sum(dy * y) with the forward's routing decisions (selection,
 // capacity, drops) fixed; they are piecewise constant.  [PithTrain] section
@@ -19,11 +19,17 @@
 //   7. gate: dl[t, idx_j] = w_j (dw_j - sum_i w_i dw_i) / tau, dWg = x^T dl,
 //      dbg = column sums of dl, dxg = dl Wg^T;
 //   8. dx[t] = sum_j dx_perm[slot[t,j]] + dxg[t].
-// The fp32 GEMMs (fp32 layers, and the gate) are one tiled kernel on the
-// vector ALUs, 64 x 64 outputs per workgroup, 4 x 4 per thread, K in steps
-// of 16 through LDS (bf16 operands widened exactly when staged); the expert
-// GEMMs of bf16 layers run on the matrix cores (bw_mfma_kernel).  Three
-// operand patterns:
+// Arithmetic.  fp32 layers: every GEMM in fp32 on the vector ALUs (one
+// tiled kernel, 64 x 64 outputs per workgroup, 4 x 4 per thread, K in steps
+// of 16 through LDS), GELU and GELU' from the device library's erff.  bf16
+// layers: the expert GEMMs run on bf16 matrix cores with fp32 accumulation
+// (the forward's pipelined 256 x 256 kernel for large problems,
+// bw_mfma_kernel otherwise); their operands g = w dy and da = dh GELU'(a)
+// are rounded to bf16 (a 2^-9 relative rounding each, like h), h is
+// recomputed in bf16 and GELU / GELU' use the forward's erf approximation
+// (Abramowitz & Stegun 7.1.26); bias gradients are column sums of the bf16 g
+// and da in fp32; the gate's GEMMs stay on the fp32 vector-ALU kernel (bf16
+// x widened exactly when staged).  Three operand patterns:
 //   NN: A rows of a segment, K-contiguous; B = W[e] [K][N]
 //   NT: A rows of a segment, K-contiguous; B = W[e] stored [N][K]
 //   TN: A and B both rows of a segment; K runs over the segment's rows
@@ -392,12 +398,16 @@ __global__ __launch_bounds__(256, MODE == BW_TN ? 4 : 1) void bw_mfma_kernel(BwG
                 if constexpr (EPI == BWE_HGRAD) {
                     const f32x4_t bb = *reinterpret_cast<const f32x4_t*>(g.bias + (int64_t)e * g.N + n);
                     v += bb;
+                    // the erf of the forward's GELU (Abramowitz & Stegun 7.1.26),
+                    // so h is rounded from the same function the forward stores
                     uint16_t hb[4];
                     f32x4_t gr;
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        hb[q] = f32_to_bf16_bits(gelu_erf(v[q]));
-                        gr[q] = gelu_grad(v[q]);
+                        float hv, ga;
+                        gelu_and_grad_as(v[q], hv, ga);
+                        hb[q] = f32_to_bf16_bits(hv);
+                        gr[q] = ga;
                     }
                     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(g.C) + ci) =
                         make_uint2(hb[0] | ((uint32_t)hb[1] << 16), hb[2] | ((uint32_t)hb[3] << 16));
@@ -660,7 +670,9 @@ static hipError_t ffn_backward_t(const BackwardArgs& b, hipStream_t st) {
             p.A = w.A; p.B = w.B; p.bias = nullptr; p.offsets = w.offsets;
             p.E = w.E; p.M = w.M; p.N = w.N; p.out = w.C;
             hipError_t err = hipSuccess;
-            if (launch_ffn_gemm_bf16_pipe(p, EPI_WGRAD, false, b.max_rows, st, &err)) return err;
+            // a segment holds each token at most once: at most min(T, max_rows) rows
+            const int64_t seg_rows = b.T < b.max_rows ? b.T : b.max_rows;
+            if (launch_ffn_gemm_bf16_pipe(p, EPI_WGRAD, false, seg_rows, st, &err)) return err;
         }
         return bwm_launch<BW_TN, BWE_WGRAD>(w, b.max_rows, st);
     };

@@ -832,6 +832,9 @@ static bool try_pipe(const GemmArgs& g, int64_t max_rows, hipStream_t st, hipErr
     const int64_t items = TN ? (int64_t)g.E * ((g.M + C::BM - 1) / C::BM) * ((g.N + C::BN - 1) / C::BN)
                              : item_bound<C>(g, max_rows);
     if (g.E > EMAX || 2 * items < (int64_t)blocks) return false;
+    // TN: buffer ranges and byte offsets over a whole segment are 32-bit
+    // (max_rows bounds a segment's rows here)
+    if (TN && max_rows * (int64_t)(g.M > g.N ? g.M : g.N) * 2 >= (int64_t(1) << 31)) return false;
     hipLaunchKernelGGL((ffn_gemm_bf16_pipe_kernel<C, NS, EMAX, WPE, EPI, AT, BKC, TN>), dim3(blocks), dim3(C::NT), 0,
                        st, g);
     *err = hipGetLastError();

@@ -120,7 +120,8 @@ static WsLayout ws_layout(const Geo& g) {
     L.w = take(sizeof(float) * (size_t)(g.T * g.k));
     L.perm = take(sizeof(int32_t) * (size_t)g.max_rows);
     L.slot = take(sizeof(int32_t) * (size_t)(g.T * g.k));
-    L.xperm = take((size_t)g.esz * (size_t)g.max_rows * g.d);
+    // row-major x_perm: fp32 layers only (a bf16 forward writes the tile copy below)
+    L.xperm = take(g.esz == 4 ? (size_t)g.esz * (size_t)g.max_rows * g.d : 0);
     // bf16: x_perm again in the h tile layout, GEMM1's operand in moe_layer_forward
     L.xpt = take(g.esz == 2 ? (size_t)g.esz * (size_t)h_tiled_rows(g.max_rows, g.E) * (size_t)((g.d + 31) / 32 * 32)
                             : 0);
@@ -228,7 +229,7 @@ int64_t moe_workspace_offset(const moe_shape* s, int which) {
         case MOE_WS_PERM: return (int64_t)L.perm;
         case MOE_WS_SLOT: return (int64_t)L.slot;
         case MOE_WS_OFFSETS: return (int64_t)L.offsets;
-        case MOE_WS_XPERM: return (int64_t)L.xperm;
+        case MOE_WS_XPERM: return g.esz == 4 ? (int64_t)L.xperm : -1;
         case MOE_WS_H: return (int64_t)L.h;
         case MOE_WS_OUT: return (int64_t)L.out;
         case MOE_WS_XPT: return (int64_t)L.xpt;
@@ -619,15 +620,15 @@ int moe_layer_forward(const moe_shape* s, const void* x, const float* Wg, const 
     da.slot = at<int32_t>(ws, L.slot);
     da.aux = aux;
     da.x = x;
-    da.x_perm = at<void>(ws, L.xperm);
+    da.x_perm = g.esz == 4 ? at<void>(ws, L.xperm) : nullptr;   // bf16: the tile copy x_pt instead
     stage_event(1, 0, st);
     MOE_HIP(launch_hist(da, st), "hist kernel launch");
     stage_event(1, 1, st);
     stage_event(2, 0, st);
     MOE_HIP(launch_scatter(da, st), "scatter kernel launch");
     stage_event(2, 1, st);
-    // bf16: x_perm row-major (the layout moe_layer_backward reads) plus the
-    // tile layout GEMM1 loads in contiguous KiBs
+    // bf16: x_perm only in the tile layout GEMM1 loads in contiguous KiBs
+    // (moe_layer_backward copies the row-major rows itself); fp32: row-major
     const bool tiled = g.esz == 2;
     stage_event(3, 0, st);
     if (tiled) MOE_HIP(launch_gather_tiled(da, at<uint16_t>(ws, L.xpt), (int)g.d, st), "gather kernel launch");

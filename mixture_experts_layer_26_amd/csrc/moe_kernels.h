@@ -90,8 +90,10 @@ inline int64_t h_tiled_rows(int64_t max_rows, int64_t E) { return ((max_rows + 1
 hipError_t launch_ffn_gemm_bf16(const GemmArgs& g, int epi, int64_t max_rows, hipStream_t st, bool a_tiled = false);
 // The pipelined 256 x 256 bf16 kernel with explicit operand layouts (the
 // backward's expert GEMMs): A row-major (not the h tile layout); B as [E, K, N]
-// or, b_kc, [E, N, K] (then K must be a multiple of 32).  Returns false and
-// launches nothing when the problem is too small for it or outside its limits.
+// or, b_kc, [E, N, K] (then K must be a multiple of 32).  max_rows bounds the
+// packed rows (EPI_WGRAD: the rows of any one expert's segment).  Returns false
+// and launches nothing when the problem is too small for it or outside its
+// limits (EPI_WGRAD: max_rows * max(M, N) * 2 >= 2^31, its 32-bit offsets).
 bool launch_ffn_gemm_bf16_pipe(const GemmArgs& g, int epi, bool b_kc, int64_t max_rows, hipStream_t st,
                                hipError_t* err);
 hipError_t launch_ffn_gemm_f32(const GemmArgs& g, int epi, hipStream_t st);

@@ -145,6 +145,26 @@ _add(MoEConfig("dense_soft_e16", T=4096, d=1024, E=16, k=16, d_ff=4096,
                capacity_factor=0.0, temperature=0.2,
                note="k = E: the soft MoE of every expert, 4096 rows each"))
 
+# several grouped-GEMM work items per workgroup at long K, compared in full:
+# K = 1536 (48 K-steps) in both GEMMs, 6 column tiles of 256 and skewed
+# expert loads (1-10 row tiles of 256 per expert) give about 970 items
+# per GEMM for 256 workgroups; the oracle still finishes every row
+_add(MoEConfig("multi_item", T=16384, d=1536, E=64, k=2, d_ff=1536,
+               capacity_factor=0.0, zipf_s=1.2, zipf_alpha=SKEW_ALPHA, bias_std=0.1,
+               note="3+ work items per workgroup at K = 1536, every row compared"))
+# the backward's weight-gradient GEMM in its pipelined form (2048 rows per
+# expert on average) with every gradient compared in full
+_add(MoEConfig("bw_long_rows", T=16384, d=512, E=16, k=2, d_ff=1024,
+               capacity_factor=0.0, bias_std=0.1, gate_bias_std=0.3,
+               note="long row segments: the weight gradients' pipelined form, full gradients"))
+
+# expert segments of 65536 rows at d_ff = 16384: a weight-gradient GEMM over
+# one segment spans 2 GiB of bf16 operand bytes, past the 32-bit offsets of
+# the pipelined weight-gradient form (the 128 x 128 kernel takes it instead)
+_add(MoEConfig("wgrad_2g", T=65536, d=16, E=2, k=2, d_ff=16384,
+               capacity_factor=0.0, bias_std=0.1,
+               note="weight-gradient segments of 2 GiB of operand bytes"))
+
 # long expert segments next to idle and one-row experts: the literal Zipf(1.2)
 # gate bias without a capacity limit gives 3 idle experts, several with 1-2
 # rows and the busiest with ~25k (the backward's weight-gradient GEMM runs

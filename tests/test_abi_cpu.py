@@ -65,11 +65,15 @@ def test_capacity_agrees_with_oracle(moe, orc):
 def test_workspace_layout(moe):
     s = moe.shape(8192, 2048, 64, 2, 8192, 2.0)
     n = moe.moe_workspace_size(s)
-    offs = [moe.moe_workspace_offset(s, w) for w in range(6)]
-    assert all(o % 256 == 0 for o in offs)
+    offs = [moe.moe_workspace_offset(s, w) for w in range(7)]
+    # a bf16 layer's forward keeps x_perm only in the tile layout: no row-major region
+    assert offs[moe.MOE_WS_XPERM] == -1
+    assert all(o % 256 == 0 for w, o in enumerate(offs) if w != moe.MOE_WS_XPERM)
     assert offs[moe.MOE_WS_H] + 16384 * 8192 * 2 <= n
-    assert offs[moe.MOE_WS_XPERM] + 16384 * 2048 * 2 <= offs[moe.MOE_WS_H]
+    assert offs[moe.MOE_WS_XPT] + 16384 * 2048 * 2 <= offs[moe.MOE_WS_H]
     assert offs[moe.MOE_WS_OUT] + 16384 * 2048 * 4 <= n
+    f32 = moe.shape(8192, 2048, 64, 2, 8192, 2.0, 1.0, 0.01, moe.MOE_F32)
+    assert moe.moe_workspace_offset(f32, moe.MOE_WS_XPERM) % 256 == 0
     assert moe.moe_workspace_offset(s, 99) == -1
 
 
@@ -83,7 +87,7 @@ def test_workspace_regions_follow_the_header(moe):
     bf16 and an fp32 layer is 256-byte aligned, the regions do not overlap and
     each holds its documented size (bf16: x_perm also in the tile layout over
     h_tiled_rows = 16 ceil((max_rows + 15 E) / 16) rows of 32 ceil(d / 32)
-    columns)."""
+    columns, and no row-major x_perm: its offset is -1)."""
     enum = _header_enum("MOE_WS_")
     assert enum and all(getattr(moe, k) == v for k, v in enum.items()), enum
     for dtype, esz in ((moe.MOE_BF16, 2), (moe.MOE_F32, 4)):
@@ -95,7 +99,10 @@ def test_workspace_regions_follow_the_header(moe):
                 moe.MOE_WS_XPERM: esz * R * d, moe.MOE_WS_OUT: 4 * R * d,
                 moe.MOE_WS_H: 2 * ht * ((F + 31) // 32 * 32) if esz == 2 else 4 * R * F,
                 moe.MOE_WS_XPT: 2 * ht * ((d + 31) // 32 * 32) if esz == 2 else 0}
-        spans = sorted((moe.moe_workspace_offset(s, w), size[w]) for w in enum.values())
+        if esz == 2:
+            assert moe.moe_workspace_offset(s, moe.MOE_WS_XPERM) == -1
+        spans = sorted((moe.moe_workspace_offset(s, w), size[w]) for w in enum.values()
+                       if not (esz == 2 and w == moe.MOE_WS_XPERM))
         assert all(o % 256 == 0 for o, _ in spans)
         for (o1, n1), (o2, _) in zip(spans, spans[1:]):
             assert o1 + n1 <= o2
@@ -204,3 +211,4 @@ def test_binding_signatures_match_header(moe):
     for name, (_, args) in moe._sigs.items():
         assert name in counts, name
         assert len(args) == counts[name], (name, len(args), counts[name])
+

@@ -6,10 +6,14 @@ the inputs, routing on the GPU's fp32 logits (the same reading as the
 forward parity).  Bars, normwise per gradient tensor:
 max|g - g_ref| <= 1e-4 max|g_ref| for fp32 layers and 1e-2 max|g_ref| for
 bf16 layers (h is stored in bf16 by the forward and recomputed so here; the
-oracle keeps it unrounded).  Small cases compare every gradient in full; at
-full size the weight gradients of the two busiest and the two least busy
-experts, dx of 64 seeded tokens, idle experts' zeros, and the sums that hold
-at any size (per-token gate gradients sum to zero)."""
+oracle keeps it unrounded).  Small cases and two mid-size cases (several
+work items per workgroup at K = 1536; long row segments, where the weight
+gradients take the pipelined form) compare every gradient in full; at full
+size the gate gradients dWg and dbg in full (the oracle's expert outputs of
+every kept row give the routing-weight gradients), the weight gradients of
+the two busiest and the two least busy experts, dx of 256 seeded tokens,
+idle experts' zeros, and the sums that hold at any size (per-token gate
+gradients sum to zero)."""
 from __future__ import annotations
 
 import numpy as np
@@ -23,6 +27,10 @@ pytestmark = pytest.mark.gpu
 TOL = {"fp32": 1e-4, "bf16": 1e-2}
 SMALL = ["tiny_fp32", "tiny_fp32_bias", "ragged_fp32", "ragged_bf16", "medium_bf16", "hybrid_small",
          "clustered_small", "single_token", "one_expert", "k_equals_e", "cap_one"]
+# every gradient in full: several items per workgroup at K = 1536; long row
+# segments (the weight gradients' pipelined form); segments whose
+# weight-gradient operands span 2 GiB (past that form's 32-bit offsets)
+MID = ["multi_item", "bw_long_rows", "wgrad_2g"]
 
 
 @pytest.fixture(scope="module")
@@ -76,8 +84,8 @@ def dy_of(cfg, seed=77):
     return np.random.default_rng(seed).standard_normal((cfg.T, cfg.d)).astype(np.float32)
 
 
-@pytest.mark.parametrize("name", SMALL)
-def test_backward_small(moe, orc, name):
+@pytest.mark.parametrize("name", SMALL + MID)
+def test_backward_every_gradient(moe, orc, name):
     cfg = get(name)
     H.log(f"[backward] {name}: T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} d_ff={cfg.d_ff} {cfg.dtype}")
     inp = make_inputs(cfg)
@@ -130,8 +138,20 @@ def test_backward_full_size(moe, orc, name):
                                                          inp["W1"], inp["b1"], inp["W2"], inp["b2"], dy, cfg.E)
         for n, ref in (("dW1", dW1), ("db1", db1), ("dW2", dW2), ("db2", db2)):
             H.assert_close_norm(got[n][e], ref[e], tol, f"{name} {n}[{e}]")
+    # gate gradients in full: the routing-weight gradient of every kept slot
+    # is dy[t] . o[row] with the oracle's expert output o of that row
+    # (dropped slots: 0)
+    kt, kj = np.nonzero(slot >= 0)
+    rows = slot[kt, kj]
+    o = orc.ffn_rows(kt.astype(np.int32), idx[kt, kj], inp["x"], inp["W1"], inp["b1"], inp["W2"], inp["b2"])
+    dw_all = np.zeros((cfg.T, cfg.k))
+    dw_all[kt, kj] = np.einsum("nd,nd->n", dy[kt].astype(np.float64), o)
+    _, dWg_ref, dbg_ref, dxg_all = orc.route_backward(inp["x"], inp["Wg"], idx, w, dw_all, cfg.temperature)
+    H.assert_close_norm(got["dWg"], dWg_ref, tol, f"{name} dWg (full)")
+    H.assert_close_norm(got["dbg"], dbg_ref, tol, f"{name} dbg (full)")
+    del o, rows
     # dx of sampled tokens: expert path plus gate path of those tokens
-    toks = H.sample_tokens(cfg.T, 64, seed=5)
+    toks = H.sample_tokens(cfg.T, 256, seed=5)
     sel = slot[toks] >= 0
     tt, jj = np.nonzero(sel)
     dw = np.zeros((len(toks), cfg.k))
@@ -140,8 +160,8 @@ def test_backward_full_size(moe, orc, name):
     dw[tt, jj] = dwr
     dx_ref = np.zeros((len(toks), cfg.d))
     np.add.at(dx_ref, tt, dxp)
-    _, _, _, dxg = orc.route_backward(inp["x"][toks], inp["Wg"], idx[toks], w[toks], dw, cfg.temperature)
-    H.assert_close_norm(got["dx"][toks], dx_ref + dxg, tol, f"{name} dx (sampled)")
+    assert np.allclose(dw, dw_all[toks], rtol=1e-9, atol=1e-12)
+    H.assert_close_norm(got["dx"][toks], dx_ref + dxg_all[toks], tol, f"{name} dx (sampled)")
     # per-token gate gradients sum to zero over the experts: so do dbg and every row of dWg
     scale = np.abs(got["dbg"]).max() + 1e-30
     assert abs(got["dbg"].sum()) <= 1e-3 * scale * np.sqrt(cfg.E)

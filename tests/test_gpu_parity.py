@@ -5,8 +5,13 @@ entry points (moe_route, moe_dispatch, moe_grouped_ffn, moe_combine,
 moe_aux_loss) run on the same seeded inputs as the oracle.  Integer outputs
 are compared bit for bit, with the routing re-derived by the oracle from
 the GPU's own fp32 logits; floating-point outputs within the tolerances of
-gpu_harness.  Small cases compare every output element; the full-size
-workloads compare every integer output and a seeded sample of token rows.
+gpu_harness.  Small cases, the 16-expert workload and the multi-item case
+compare every output element.  The other full-size workloads compare every
+integer output in full; of the expert outputs (out_perm) the first and last
+row of every 64-row block of every expert segment (so the first and last row
+of every grouped-GEMM work item, whatever its row tile), every row of the two
+busiest and the two least busy active experts, and the rows of 1024 seeded
+tokens, whose y is compared too.
 """
 from __future__ import annotations
 
@@ -22,10 +27,11 @@ SMALL = ["tiny_fp32", "tiny_fp32_bias", "ragged_bf16", "ragged_fp32", "medium_bf
          "hybrid_small", "clustered_small", "single_token", "one_expert", "k_equals_e",
          "cap_one", "max_experts", "max_k", "soft_k_equals_e12", "k16_e40", "e100_k5",
          "e200_t33001"]
-FULL = ["bf16_e16", "skewed_e64", "skewed_e64_literal", "hybrid_e128", "large_e256", "dense_soft_e16", "ragged_large",
-        "ragged_large_even"]
-FULL_Y = {"bf16_e16"}          # oracle over every token still takes seconds
-SAMPLE = 160                   # token rows checked on the other full-size cases
+FULL = ["bf16_e16", "multi_item", "skewed_e64", "skewed_e64_literal", "hybrid_e128", "large_e256", "dense_soft_e16",
+        "ragged_large", "ragged_large_even"]
+FULL_Y = {"bf16_e16", "multi_item"}   # the oracle over every token still takes seconds
+SAMPLE = 1024                  # tokens whose y is checked on the other full-size cases
+BLOCK = 64                     # row blocks of an expert segment whose first and last rows are checked
 
 
 @pytest.fixture(scope="module")
@@ -38,6 +44,28 @@ def moe():
 
 def _expert_of_rows(offsets, rows):
     return (np.searchsorted(offsets, rows, side="right") - 1).astype(np.int32)
+
+
+def item_rows(offsets, block=BLOCK):
+    """First and last row of every `block`-row block of every expert segment
+    (a superset of the first and last rows of the GEMMs' work items for any
+    row tile that is a multiple of `block`)."""
+    rows = []
+    for e in range(len(offsets) - 1):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        for m0 in range(lo, hi, block):
+            rows += [m0, min(m0 + block, hi) - 1]
+    return np.unique(np.asarray(rows, np.int64))
+
+
+def hot_cold_rows(counts, offsets, n=2):
+    """Every row of the n busiest and the n least busy active experts."""
+    act = np.nonzero(counts > 0)[0]
+    order = act[np.argsort(counts[act], kind="stable")]
+    pick = sorted(set(order[:n].tolist()) | set(order[-n:].tolist()))
+    if not pick:
+        return np.zeros(0, np.int64)
+    return np.concatenate([np.arange(offsets[e], offsets[e + 1], dtype=np.int64) for e in pick])
 
 
 def _check_case(moe, orc, name):
@@ -120,20 +148,28 @@ def _check_case(moe, orc, name):
     S = int(dsp["offsets"][-1])
     xp = H.to_host(xperm)
     assert np.array_equal(xp[:S], inp["x"].view(xp.dtype)[dsp["perm"][:S]]), f"{name}: x_perm rows"
-    # FFN rows: all of them for the small cases, those of the sampled tokens otherwise
-    if name in SMALL:
+    # FFN rows: all of them for the small cases and FULL_Y; otherwise the
+    # first and last row of every work item, the busiest and least busy
+    # experts in full and the rows of the sampled tokens
+    if name in SMALL or name in FULL_Y:
         rows = np.arange(S, dtype=np.int64)
     else:
         sl = dsp["slot"][toks]
-        rows = np.unique(sl[sl >= 0]).astype(np.int64)
+        rows = np.unique(np.concatenate([sl[sl >= 0].astype(np.int64), item_rows(dsp["offsets"]),
+                                         hot_cold_rows(dsp["counts"], dsp["offsets"])]))
     oref = orc.ffn_rows(dsp["perm"][rows], _expert_of_rows(dsp["offsets"], rows), inp["x"],
                         inp["W1"], inp["b1"], inp["W2"], inp["b2"])
     H.assert_close_norm(H.to_host(out_perm)[rows], oref, tol_y, f"{name} grouped FFN rows")
+    # the fused forward's expert outputs (its first GEMM reads the tiled copy of x_perm)
+    off_out = moe.moe_workspace_offset(s, moe.MOE_WS_OUT)
+    out_fused = wsh[off_out:off_out + 4 * smax * d].view(np.float32).reshape(smax, d)
+    assert np.array_equal(out_fused[:S], H.to_host(out_perm)[:S]), f"{name}: fused and unfused expert outputs"
     H.assert_close_norm(H.to_host(y2)[toks], yref, tol_y, f"{name} unfused y")
     # the fused entry point runs the same kernels as the separate ones
     assert np.array_equal(H.to_host(y2), yh), f"{name}: fused and unfused y differ"
     assert abs(float(H.to_host(aux2)[0]) - aux_ref) <= H.TOL_AUX * abs(aux_ref) + 1e-12
-    H.log(f"[parity] {name}: ok  logits {gerr:.2e}  w {werr:.2e}  y {yerr:.2e}  S={S}/{T * k}")
+    H.log(f"[parity] {name}: ok  logits {gerr:.2e}  w {werr:.2e}  y {yerr:.2e}  S={S}/{T * k}  "
+          f"rows checked {len(rows)}  tokens {len(toks)}")
     del dv, ws, xperm, out_perm
     torch.cuda.empty_cache()
 
