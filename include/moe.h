@@ -175,6 +175,25 @@ int moe_dispatch(const moe_shape* s, const void* x, const int32_t* topk_idx,
                  int32_t* perm, int32_t* slot, void* x_perm,
                  void* ws, size_t ws_bytes, void* stream);
 
+/* 2b. moe_dispatch without a workspace, for callers that cannot allocate
+ *     device memory (code under stream capture, tight serving loops,
+ *     harnesses that forbid hipMalloc).  Same arguments and outputs as
+ *     moe_dispatch, bit for bit, minus ws: the per-block expert histogram
+ *     (int32 [nblk][E], nblk = the dispatch's token blocks of at least 64
+ *     tokens each) lives in a static device array of
+ *     MOE_NOALLOC_SCRATCH_BYTES that every GPU the library runs on holds
+ *     until the process ends.  Any shape with E * ceil(T/64) <= 2^20 fits;
+ *     a shape whose histogram does not fit returns MOE_ERR_WORKSPACE and
+ *     launches nothing.  The first call on a device looks up the array's
+ *     address there (hipGetSymbolAddress); no call allocates device or host
+ *     memory.  Every call on one GPU shares the array: calls that overlap on
+ *     one GPU (other streams, other threads) race and give undefined
+ *     results; calls ordered on one stream are safe. */
+#define MOE_NOALLOC_SCRATCH_BYTES (4u << 20)
+int moe_dispatch_noalloc(const moe_shape* s, const void* x, const int32_t* topk_idx,
+                         int32_t* routed /* NULL ok */, int32_t* counts, int32_t* offsets,
+                         int32_t* perm, int32_t* slot, void* x_perm, void* stream);
+
 /* 3. Grouped expert FFN over the packed rows: for every row r of expert e
  *    (offsets[e] <= r < offsets[e+1]),
  *      out_perm[r] = GELU(x_perm[r] W1[e] + b1[e]) W2[e] + b2[e]

@@ -61,6 +61,7 @@ _sigs = {
     "moe_route": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "moe_route_logits": (C.c_int, [_SP, _P, _P, _P, _P]),
     "moe_dispatch": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "moe_dispatch_noalloc": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_grouped_ffn": (C.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "moe_combine": (C.c_int, [_SP, _P, _P, _P, _P, _P]),
     "moe_aux_loss": (C.c_int, [_SP, _P, _P, _P]),
@@ -160,6 +161,14 @@ def moe_dispatch(s, x, topk_idx, routed, counts, offsets, perm, slot, x_perm, ws
     _check(_lib.moe_dispatch(C.byref(s), _ptr(x), _ptr(topk_idx), _ptr(routed), _ptr(counts),
                              _ptr(offsets), _ptr(perm), _ptr(slot), _ptr(x_perm), _ptr(ws),
                              ws.numel() * ws.element_size(), _stream(stream)))
+
+
+MOE_NOALLOC_SCRATCH_BYTES = 4 << 20
+
+
+def moe_dispatch_noalloc(s, x, topk_idx, routed, counts, offsets, perm, slot, x_perm, stream=None) -> None:
+    _check(_lib.moe_dispatch_noalloc(C.byref(s), _ptr(x), _ptr(topk_idx), _ptr(routed), _ptr(counts),
+                                     _ptr(offsets), _ptr(perm), _ptr(slot), _ptr(x_perm), _stream(stream)))
 
 
 def moe_grouped_ffn(s, x_perm, offsets, W1, b1, W2, b2, out_perm, ws, stream=None) -> None:

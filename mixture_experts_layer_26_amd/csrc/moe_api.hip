@@ -11,6 +11,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -162,6 +163,33 @@ static int check_ws(const Geo& g, void* ws, size_t ws_bytes, WsLayout* L) {
 template <typename T>
 static T* at(void* ws, size_t off) {
     return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+// ---- static scratch of moe_dispatch_noalloc --------------------------------
+// The dispatch's per-block expert histogram [nblk][E] int32 for callers that
+// cannot allocate: a file-scope device array that every GPU the library runs
+// on holds until the process ends.  In host code `scratch` names a host-side
+// stand-in, not a device address: its address on each device comes from
+// hipGetSymbolAddress, taken once per device with that device current, and
+// only that pointer is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_dev[64];   // device address of `scratch`, per device
+
+static int scratch_on_current_device(void** out) {
+    int dev = 0;
+    MOE_HIP(hipGetDevice(&dev), "hipGetDevice");
+    if (dev < 0 || dev >= 64) return fail(MOE_ERR_UNSUPPORTED, "device %d: the scratch table holds 64 devices", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_dev[dev] == nullptr) {
+        void* p = nullptr;
+        MOE_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+        if (p == nullptr) return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch_dev[dev] = p;
+    }
+    *out = g_scratch_dev[dev];
+    return MOE_OK;
 }
 
 static const char* kStageNames[] = {"route", "hist", "scatter", "gather", "ffn1", "ffn2", "combine"};
@@ -326,6 +354,44 @@ int moe_dispatch(const moe_shape* s, const void* x, const int32_t* topk_idx, int
     DispatchArgs a = dispatch_args(g, s);
     a.idx = topk_idx;
     a.blkhist = at<int32_t>(ws, L.blkhist);
+    a.routed = routed;
+    a.counts = counts;
+    a.offsets = offsets;
+    a.perm = perm;
+    a.slot = slot;
+    a.x = x;
+    a.x_perm = x_perm;
+    MOE_HIP(launch_hist(a, st), "hist kernel launch");
+    MOE_HIP(launch_scatter(a, st), "scatter kernel launch");
+    MOE_HIP(launch_gather(a, st), "gather kernel launch");
+    return MOE_OK;
+}
+
+int moe_dispatch_noalloc(const moe_shape* s, const void* x, const int32_t* topk_idx, int32_t* routed,
+                         int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* slot, void* x_perm,
+                         void* stream) {
+    Geo g;
+    if (int rc = validate(s, &g)) return rc;
+    MOE_REQUIRE(x);
+    MOE_REQUIRE(topk_idx);
+    MOE_OPTIONAL(routed);
+    MOE_REQUIRE(counts);
+    MOE_REQUIRE(offsets);
+    MOE_REQUIRE(perm);
+    MOE_REQUIRE(slot);
+    MOE_REQUIRE(x_perm);
+    const size_t need = sizeof(int32_t) * (size_t)g.nblk * (size_t)g.E;
+    if (need > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
+        return fail(MOE_ERR_WORKSPACE,
+                    "moe_dispatch_noalloc: the histogram of %d token blocks x %lld experts needs %zu bytes, above "
+                    "the %zu-byte static scratch (T=%lld); use moe_dispatch with a workspace",
+                    g.nblk, (long long)g.E, need, (size_t)MOE_NOALLOC_SCRATCH_BYTES, (long long)g.T);
+    void* sp = nullptr;
+    if (int rc = scratch_on_current_device(&sp)) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    DispatchArgs a = dispatch_args(g, s);
+    a.idx = topk_idx;
+    a.blkhist = static_cast<int32_t*>(sp);   // every entry [b][e] is written by this call's hist launch
     a.routed = routed;
     a.counts = counts;
     a.offsets = offsets;

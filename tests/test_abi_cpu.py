@@ -212,3 +212,24 @@ def test_binding_signatures_match_header(moe):
         assert name in counts, name
         assert len(args) == counts[name], (name, len(args), counts[name])
 
+
+def test_dispatch_noalloc_rejects_histograms_past_its_scratch(moe):
+    """moe_dispatch_noalloc keeps its per-block histogram in a static array of
+    MOE_NOALLOC_SCRATCH_BYTES; a shape whose histogram needs more (1024
+    experts over 2^20 tokens: 4096 blocks of 256 tokens, 16 MiB) is refused
+    on the host with MOE_ERR_WORKSPACE before any device work, so aligned
+    stand-in pointers are never touched."""
+    import ctypes as C
+    assert moe.MOE_NOALLOC_SCRATCH_BYTES == _header_define("MOE_NOALLOC_SCRATCH_BYTES")
+    s = moe.shape(1 << 20, 64, 1024, 2, 64, 1.0)
+    p = 1 << 20
+    rc = moe._lib.moe_dispatch_noalloc(C.byref(s), p, p, None, p, p, p, p, p, 0)
+    assert rc == 5, rc   # MOE_ERR_WORKSPACE
+    msg = moe._lib.moe_last_error().decode()
+    assert "static scratch" in msg and "16777216 bytes" in msg, msg
+
+
+def _header_define(name):
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    m = re.search(r"#define\s+%s\s+\((\d+)u\s*<<\s*(\d+)\)" % name, src)
+    return int(m.group(1)) << int(m.group(2))
