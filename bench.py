@@ -11,8 +11,14 @@ the library records around each of its launches inside that same timed
 region.  Prints one JSON line.
 
 The default workload is the E=64, top-2, d=2048 layer (T=8192, d_ff=8192,
-capacity factor 2, Zipf-skewed gate).  The oracle (CPU) is timed beside it
-on a bounded sample of the same workload.
+capacity factor 2, Zipf-skewed gate); `value` is its tokens/s.  The oracle
+(CPU) is timed beside it on the same workload (the whole batch when it fits
+the time budget).  Unless --only is given, every other workload (the tiny
+fp32 layer, the 16-, 128- and 256-expert layers and the literal-Zipf reading
+of the headline) is then timed the same way with shorter runs and reported
+under "configs": ms/step, tokens/s, the grouped GEMMs' rate, the dominant
+launch against its roofline and the routing / permutation / combine launches
+against HBM.
 """
 from __future__ import annotations
 
@@ -76,8 +82,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--config", default=None)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="budget of the oracle's expert-FFN sample")
+    ap.add_argument("--cpu-seconds", type=float, default=30.0,
+                    help="time budget of the oracle: the whole workload when it fits, else a scaled sample")
+    ap.add_argument("--only", action="store_true",
+                    help="time the one workload only (no per-workload summary of the others)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
     ap.add_argument("--no-peaks", action="store_true",
@@ -120,11 +128,24 @@ def stage_bytes_flops(cfg, S, active, esz, nblk):
     }
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(cfg, inp, budget_s):
-    """Time the oracle (as it stands) on a bounded sample of the workload:
-    gate, routing and dispatch over all tokens, then the expert FFN and
-    combine over leading token chunks until the time budget is spent; the
-    FFN time is scaled to all kept slots."""
+    """Time the oracle (as it stands) over the whole workload when it fits
+    the time budget: the full layer forward (gate, routing, dispatch, every
+    kept slot's expert FFN, combine and the balance loss) in one call.  If a
+    first timed chunk shows that the whole batch would take more than
+    budget_s, the expert FFN and combine run over leading token chunks until
+    the budget is spent and are scaled to all kept slots (said in `sample`)."""
     import numpy as np
     import oracle
     x, Wg, bg = inp["x"], inp["Wg"], inp["bg"]
@@ -135,7 +156,23 @@ def cpu_baseline(cfg, inp, budget_s):
     dsp = oracle.dispatch(idx, cfg.E, cap)
     t_route = time.perf_counter() - t0
     S = int(dsp["offsets"][-1])
-    done_tok, done_slots, t_ffn = 0, 0, 0.0
+    # a first chunk sizes the rest
+    probe = np.arange(0, min(cfg.T, 256), dtype=np.int32)
+    t1 = time.perf_counter()
+    oracle.layer_tokens(probe, x, inp["W1"], inp["b1"], inp["W2"], inp["b2"], idx, dsp["slot"], w)
+    t_probe = time.perf_counter() - t1
+    probe_slots = max(int((dsp["slot"][probe] >= 0).sum()), 1)
+    base = {"unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle", "cpu_model": cpu_model()}
+    if t_probe * S / probe_slots <= budget_s:
+        t2 = time.perf_counter()
+        ref = oracle.layer_forward(x, Wg, bg, inp["W1"], inp["b1"], inp["W2"], inp["b2"], cfg.k,
+                                   cfg.capacity_factor, cfg.temperature, cfg.aux_lambda)
+        total = time.perf_counter() - t2
+        return dict(base, value=cfg.T / total, seconds_measured=round(total, 2), sample=(
+            f"the whole workload: one oracle layer forward (gate, top-k, dispatch, expert FFN of all "
+            f"{int(ref['offsets'][-1])} kept slots, combine, balance loss) over all {cfg.T} tokens, "
+            f"{total:.2f} s; fp64, plain C + OpenMP on {oracle.threads()} threads"))
+    done_tok, done_slots, t_ffn = int(probe[-1]) + 1, probe_slots, t_probe
     chunk = 64
     while done_tok < cfg.T and t_ffn < budget_s:
         toks = np.arange(done_tok, min(cfg.T, done_tok + chunk), dtype=np.int32)
@@ -145,13 +182,10 @@ def cpu_baseline(cfg, inp, budget_s):
         done_slots += int((dsp["slot"][toks] >= 0).sum())
         done_tok = int(toks[-1]) + 1
     total = t_route + t_ffn * (S / max(done_slots, 1))
-    return {
-        "value": cfg.T / total, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
-        "sample": (f"gate+top-k+dispatch over all {cfg.T} tokens ({t_route:.2f} s); expert FFN + "
-                   f"combine over the first {done_tok} tokens ({done_slots} of {S} kept slots, "
-                   f"{t_ffn:.2f} s), scaled to all {S} slots; fp64, plain C + OpenMP"),
-        "seconds_measured": round(t_route + t_ffn, 2),
-    }
+    return dict(base, value=cfg.T / total, seconds_measured=round(t_route + t_ffn, 2), sample=(
+        f"gate+top-k+dispatch over all {cfg.T} tokens ({t_route:.2f} s); expert FFN + combine over the "
+        f"first {done_tok} tokens ({done_slots} of {S} kept slots, {t_ffn:.2f} s), scaled by {S}/{done_slots} "
+        f"to all kept slots; fp64, plain C + OpenMP on {oracle.threads()} threads"))
 
 
 def _stage_of(kernel: str):
@@ -393,25 +427,12 @@ def time_backward(moe, s, cfg, d, ws, stream, reps=5):
                       else "fp32 vector ALUs")}
 
 
-def main():
-    args = parse()
-    if args.traffic_from:
-        from moe_inputs import HEADLINE
-        write_traffic(*args.traffic_from, args.config or HEADLINE, args.steps)
-        return
-    if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
-                          "n_gpus": args.gpus}), flush=True)
-        sys.exit(2)
+def prepare(moe, cfg, dev):
+    """Seeded inputs of the workload on the device, its shape, workspace and
+    outputs; returns (host inputs, device inputs, buffers, seconds taken)."""
     import numpy as np
     import torch
-
-    import mixture_experts_layer_26_amd as moe
-    from moe_inputs import HEADLINE, get, make_inputs
-
-    cfg = get(args.config or HEADLINE)
-    torch.cuda.set_device(0)
-    dev = torch.device("cuda:0")
+    from moe_inputs import make_inputs
     t_gen = time.perf_counter()
     inp = make_inputs(cfg)
 
@@ -423,38 +444,43 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
     d = {k: to_dev(v) for k, v in inp.items()}
-    esz = 2 if cfg.dtype == "bf16" else 4
     s = moe.shape(cfg.T, cfg.d, cfg.E, cfg.k, cfg.d_ff, cfg.capacity_factor, cfg.temperature,
                   cfg.aux_lambda, moe.MOE_BF16 if cfg.dtype == "bf16" else moe.MOE_F32)
-    ws = moe.workspace(s, dev)
-    y = torch.empty((cfg.T, cfg.d), dtype=torch.float32, device=dev)
-    counts = torch.empty(cfg.E, dtype=torch.int32, device=dev)
-    routed = torch.empty(cfg.E, dtype=torch.int32, device=dev)
-    aux = torch.empty(1, dtype=torch.float32, device=dev)
+    b = dict(s=s, ws=moe.workspace(s, dev),
+             y=torch.empty((cfg.T, cfg.d), dtype=torch.float32, device=dev),
+             counts=torch.empty(cfg.E, dtype=torch.int32, device=dev),
+             routed=torch.empty(cfg.E, dtype=torch.int32, device=dev),
+             aux=torch.empty(1, dtype=torch.float32, device=dev))
     torch.cuda.synchronize()
-    t_gen = time.perf_counter() - t_gen
-    stream = torch.cuda.current_stream()
+    return inp, d, b, time.perf_counter() - t_gen
+
+
+def time_forward(moe, cfg, d, b, stream, steps, warmup):
+    """W untimed steps, then K timed steps between two synchronisations on
+    the launch stream.  The timed steps record HIP events around the two
+    expert GEMMs only (the dominant launches, whose times the roofline needs
+    from the timed region); every event record between launches costs about
+    2 us, so the other stages are timed in a second, fully instrumented pass
+    of as many steps right after.  Returns (ms per step, {stage: us})."""
+    import numpy as np
+    import torch
+    s, ws = b["s"], b["ws"]
 
     def step(events=None):
         if events is not None:
             moe.moe_set_stage_events(events)
-        moe.moe_layer_forward(s, d["x"], d["Wg"], d["bg"], d["W1"], d["b1"], d["W2"], d["b2"], y,
-                              counts, aux, ws, routed=routed, stream=stream)
+        moe.moe_layer_forward(s, d["x"], d["Wg"], d["bg"], d["W1"], d["b1"], d["W2"], d["b2"], b["y"],
+                              b["counts"], b["aux"], ws, routed=b["routed"], stream=stream)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     names = moe.moe_stage_names()
-    # The timed steps record HIP events around the two expert GEMMs only (the
-    # dominant launches, whose times the roofline needs from the timed
-    # region); every event record between launches costs about 2 us, so the
-    # other stages are timed in a second, fully instrumented pass of as many
-    # steps right after.
     gemm_stages = {j for j, n in enumerate(names) if n in ("ffn1", "ffn2")}
 
     def make_events(which):
         ev = [[torch.cuda.Event(enable_timing=True) if (i // 2) in which else None
-               for i in range(2 * len(names))] for _ in range(args.steps)]
+               for i in range(2 * len(names))] for _ in range(steps)]
         for e in ev:                  # torch creates the HIP event handles lazily on record
             for x in e:
                 if x is not None:
@@ -466,12 +492,12 @@ def main():
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
-    for i in range(args.steps):
+    for i in range(steps):
         step(ev_timed[i])
     stop.record(stream)
     torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / args.steps
-    for i in range(args.steps):
+    ms = start.elapsed_time(stop) / steps
+    for i in range(steps):
         step(ev_all[i])
     torch.cuda.synchronize()
     moe.moe_set_stage_events([None] * (2 * len(names)))
@@ -479,13 +505,19 @@ def main():
     def stage_mean(ev, j):
         return 1e3 * float(np.mean([e[2 * j].elapsed_time(e[2 * j + 1]) for e in ev]))
 
-    stage_us = {n: stage_mean(ev_timed if j in gemm_stages else ev_all, j) for j, n in enumerate(names)}
+    return ms, {n: stage_mean(ev_timed if j in gemm_stages else ev_all, j) for j, n in enumerate(names)}
 
-    c = counts.cpu().numpy()
-    rt = routed.cpu().numpy()
+
+def summarize(cfg, ms, stage_us, b):
+    """Throughput, the grouped GEMMs' rate, the dominant launch against its
+    roofline and the routing / permutation / combine launches against HBM."""
+    c = b["counts"].cpu().numpy()
+    rt = b["routed"].cpu().numpy()
+    esz = 2 if cfg.dtype == "bf16" else 4
     S = int(c.sum())
     active = int((c > 0).sum())
-    nblk = (cfg.T + dispatch_block_tokens(cfg.T, cfg.E, cfg.k) - 1) // dispatch_block_tokens(cfg.T, cfg.E, cfg.k)
+    bt = dispatch_block_tokens(cfg.T, cfg.E, cfg.k)
+    nblk = (cfg.T + bt - 1) // bt
     bf = stage_bytes_flops(cfg, S, active, esz, nblk)
     ffn_flops = 4 * S * cfg.d * cfg.d_ff
     gemm_us = stage_us["ffn1"] + stage_us["ffn2"]
@@ -493,8 +525,7 @@ def main():
     dbytes, dflops = bf[dom]
     t_dom = stage_us[dom] * 1e-6
     peak_mm = PEAK_BF16 if esz == 2 else PEAK_FP32
-    hbm_bound = dbytes / PEAK_HBM >= dflops / peak_mm
-    if hbm_bound:
+    if dbytes / PEAK_HBM >= dflops / peak_mm:
         roof = {"bound": "hbm", "achieved": dbytes / t_dom / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
     else:
         roof = {"bound": "mfma", "achieved": dflops / t_dom / 1e12, "peak": peak_mm / 1e12,
@@ -506,31 +537,14 @@ def main():
     roof["algorithmic_flops"] = dflops
     roof["mfma_frac"] = dflops / t_dom / peak_mm
     roof["hbm_frac"] = dbytes / t_dom / PEAK_HBM
-
-    out = {
-        "metric": METRIC,
-        "value": cfg.T / (ms * 1e-3),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+    return {
         "ms_per_step": ms,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": cfg.dtype,
-        "data": "synthetic (seeded numpy PCG64 inputs of the workload's shape and distributions)",
-        "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k,
-                   "d_ff": cfg.d_ff, "capacity_factor": cfg.capacity_factor,
-                   "temperature": cfg.temperature, "seed": cfg.seed,
-                   "gate_bias": (f"zipf s={cfg.zipf_s} alpha={cfg.zipf_alpha}" if cfg.zipf_s else None),
-                   "parallelism": "single GPU"},
+        "tokens_per_s": cfg.T / (ms * 1e-3),
         "roofline": roof,
         "grouped_gemm": {"tflops": ffn_flops / (gemm_us * 1e-6) / 1e12,
-                         "frac_peak_bf16": ffn_flops / (gemm_us * 1e-6) / peak_mm, "us": gemm_us},
+                         "frac_peak_bf16" if esz == 2 else "frac_peak_fp32": ffn_flops / (gemm_us * 1e-6) / peak_mm,
+                         "us": gemm_us},
         "stages_us": stage_us,
-        "stages_timing": "ffn1/ffn2: HIP events inside the timed steps; other stages: a second pass of the same "
-                         "number of steps with events around every launch",
         # algorithmic bytes of the routing, permutation and combine launches
         # over their HIP-event times (which include the event records: a few
         # us on these short launches, see the kernel trace in profiles/)
@@ -541,9 +555,62 @@ def main():
         "layer_tflops": (ffn_flops + 2 * cfg.T * cfg.d * cfg.E) / (ms * 1e-3) / 1e12,
         "kept_slots": S, "dropped_slots": cfg.T * cfg.k - S, "active_experts": active,
         "routed_cv": float(rt.std() / rt.mean()),
-        "aux": float(aux.cpu().numpy()[0]),
+        "aux": float(b["aux"].cpu().numpy()[0]),
+    }
+
+
+def config_of(cfg):
+    return {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k,
+            "d_ff": cfg.d_ff, "capacity_factor": cfg.capacity_factor,
+            "temperature": cfg.temperature, "seed": cfg.seed, "dtype": cfg.dtype,
+            "gate_bias": (f"zipf s={cfg.zipf_s} alpha={cfg.zipf_alpha}" if cfg.zipf_s else None),
+            "clustered_tokens": cfg.cluster_frac or None,
+            "parallelism": "single GPU"}
+
+
+def main():
+    args = parse()
+    if args.traffic_from:
+        from moe_inputs import HEADLINE
+        write_traffic(*args.traffic_from, args.config or HEADLINE, args.steps)
+        return
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+    import torch
+
+    import mixture_experts_layer_26_amd as moe
+    from moe_inputs import HEADLINE, WORKLOADS, get
+
+    cfg = get(args.config or HEADLINE)
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    inp, d, b, t_gen = prepare(moe, cfg, dev)
+    ms, stage_us = time_forward(moe, cfg, d, b, stream, args.steps, args.warmup)
+    summ = summarize(cfg, ms, stage_us, b)
+    out = {
+        "metric": METRIC,
+        "value": summ["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded numpy PCG64 inputs of the workload's shape and distributions)",
+        "config": config_of(cfg),
+        "roofline": summ["roofline"],
+        "stages_timing": "ffn1/ffn2: HIP events inside the timed steps; other stages: a second pass of the same "
+                         "number of steps with events around every launch",
         "setup_seconds": round(t_gen, 2),
     }
+    out.update({k: v for k, v in summ.items() if k not in ("ms_per_step", "tokens_per_s", "roofline")})
+    s, ws, y, counts, aux = b["s"], b["ws"], b["y"], b["counts"], b["aux"]
     out["heat_map"] = time_heat_map(moe, s, cfg, d, y, counts, aux, ws, stream)
     out["router_variant"] = time_router_variant(moe, s, cfg, d, ws, stream)
     if not args.no_backward:
@@ -555,10 +622,29 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         out["copy_calib_bytes"] = COPY_CALIB_BYTES
+    S, active = summ["kept_slots"], summ["active_experts"]
     if not args.no_peaks and not args.copy_calib:
         out["measured_peaks"] = measured_peaks(cfg, S, active, dev)
+    del d, b, s, ws, y, counts, aux
+    torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
+    del inp
+    if not args.only:
+        # every other workload (and the literal-Zipf reading of the headline):
+        # the same timed forward, shorter runs, no backward or oracle
+        out["configs"] = {}
+        for name in WORKLOADS + ["skewed_e64_literal"]:
+            if name == cfg.name:
+                continue
+            c2 = get(name)
+            _, d2, b2, tg = prepare(moe, c2, dev)
+            w2, k2 = min(args.warmup, 10), min(args.steps, 20)
+            ms2, st2 = time_forward(moe, c2, d2, b2, stream, k2, w2)
+            out["configs"][name] = dict(config=config_of(c2), steps=k2, warmup=w2, dtype=c2.dtype,
+                                        **summarize(c2, ms2, st2, b2), setup_seconds=round(tg, 2))
+            del d2, b2
+            torch.cuda.empty_cache()
     print(json.dumps(out), flush=True)
 
 

@@ -85,6 +85,9 @@ struct TileCfg {
 #endif
 using TileSmall = TileCfg<MOE_TILE_SMALL>;
 using TilePipe = TileCfg<MOE_TILE_PIPE>;
+#ifndef MOE_PIPE_NS
+#define MOE_PIPE_NS 4   // LDS ring slots of the pipelined kernel
+#endif
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
@@ -844,7 +847,7 @@ static bool try_pipe(const GemmArgs& g, int64_t max_rows, hipStream_t st, hipErr
 template <int EPI, bool AT = kATiled<EPI>>
 static hipError_t launch_epi(const GemmArgs& g, int64_t max_rows, hipStream_t st) {
     hipError_t err = hipSuccess;
-    if (try_pipe<TilePipe, 4, 1024, TilePipe::NW >= 8 ? 2 : 1, EPI, AT>(g, max_rows, st, &err)) return err;
+    if (try_pipe<TilePipe, MOE_PIPE_NS, 1024, TilePipe::NW >= 8 ? 2 : 1, EPI, AT>(g, max_rows, st, &err)) return err;
     hipLaunchKernelGGL((ffn_gemm_bf16_kernel<TileSmall, EPI, AT>), dim3(small_blocks<TileSmall, EPI, AT>()),
                        dim3(TileSmall::NT), 0, st, g);
     return hipGetLastError();
@@ -860,12 +863,12 @@ bool launch_ffn_gemm_bf16_pipe(const GemmArgs& g, int epi, bool b_kc, int64_t ma
                                hipError_t* err) {
     constexpr int WPE = TilePipe::NW >= 8 ? 2 : 1;
     if (b_kc && g.K % BK != 0) return false;   // both operands K-contiguous: no zero rows under a K tail
-    if (epi == EPI_HGRAD && !b_kc) return try_pipe<TilePipe, 4, 1024, WPE, EPI_HGRAD, false, false>(g, max_rows, st, err);
+    if (epi == EPI_HGRAD && !b_kc) return try_pipe<TilePipe, MOE_PIPE_NS, 1024, WPE, EPI_HGRAD, false, false>(g, max_rows, st, err);
     if (epi == EPI_STORE_F32 && b_kc)
-        return try_pipe<TilePipe, 4, 1024, WPE, EPI_STORE_F32, false, true>(g, max_rows, st, err);
-    if (epi == EPI_DA && b_kc) return try_pipe<TilePipe, 4, 1024, WPE, EPI_DA, false, true>(g, max_rows, st, err);
+        return try_pipe<TilePipe, MOE_PIPE_NS, 1024, WPE, EPI_STORE_F32, false, true>(g, max_rows, st, err);
+    if (epi == EPI_DA && b_kc) return try_pipe<TilePipe, MOE_PIPE_NS, 1024, WPE, EPI_DA, false, true>(g, max_rows, st, err);
     if (epi == EPI_WGRAD && !b_kc)
-        return try_pipe<TilePipe, 4, 1024, WPE, EPI_WGRAD, false, false, true>(g, max_rows, st, err);
+        return try_pipe<TilePipe, MOE_PIPE_NS, 1024, WPE, EPI_WGRAD, false, false, true>(g, max_rows, st, err);
     return false;
 }
 

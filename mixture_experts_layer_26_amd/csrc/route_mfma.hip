@@ -352,6 +352,9 @@ static void launch_bm(const RouteArgs& a, const uint16_t* W3, hipStream_t st) {
 #ifndef MOE_ROUTE_NW
 #define MOE_ROUTE_NW 8   // waves per workgroup up to 64 experts
 #endif
+#ifndef MOE_ROUTE_BM64_MIN
+#define MOE_ROUTE_BM64_MIN 256   // 64-token tiles from this many workgroups per 256 CUs
+#endif
 
 template <int EP2>
 static void launch_ep2(const RouteArgs& a, const uint16_t* W3, int cus, hipStream_t st) {
@@ -365,7 +368,7 @@ static void launch_ep2(const RouteArgs& a, const uint16_t* W3, int cus, hipStrea
         launch_bm<EP2, 64, 4, 2, MOE_ROUTE_NW>(a, W3, st);
     } else {
         // 64-token tiles halve the weight traffic per token once they still fill the CUs
-        if ((a.T + 63) / 64 >= cus) launch_bm<EP2, 64, 4, 2, MOE_ROUTE_NW>(a, W3, st);
+        if ((a.T + 63) / 64 >= MOE_ROUTE_BM64_MIN * cus / 256) launch_bm<EP2, 64, 4, 2, MOE_ROUTE_NW>(a, W3, st);
         else launch_bm<EP2, 32, 4, 2, MOE_ROUTE_NW>(a, W3, st);
     }
 }
