@@ -349,6 +349,54 @@ def _median_us(fn, stream, reps=20):
     return 1e3 * float(np.median([a.elapsed_time(b) for a, b in ev]))
 
 
+def time_combine_cold(moe, s, cfg, b, stream, reps=10):
+    """The combine alone (moe_combine on the forward's expert outputs, slot
+    and weights), once right after a forward (out_perm written just before,
+    partly still in the 256 MB MALL) and once after 1 GiB has been streamed
+    through the caches (a device copy, each rep), so that out_perm comes from
+    HBM.  Algorithmic bytes as the combine stage: read the kept rows' fp32
+    outputs and the weights, write y."""
+    import numpy as np
+    import torch
+    dev = b["y"].device
+    T, D, k = cfg.T, cfg.d, cfg.k
+    f32, i32 = torch.float32, torch.int32
+    idx, w = torch.empty((T, k), dtype=i32, device=dev), torch.empty((T, k), dtype=f32, device=dev)
+    ws = b["ws"]
+    R = moe.moe_max_rows(s)
+
+    def region(which, dtype, n, esz):
+        off = moe.moe_workspace_offset(s, which)
+        return ws[off:off + n * esz].view(dtype)
+
+    y2 = torch.empty((T, D), dtype=f32, device=dev)
+    src = torch.empty(COPY_CALIB_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    warm, cold = [], []
+    for _ in range(reps):
+        moe.moe_layer_forward(s, b["d"]["x"], b["d"]["Wg"], b["d"]["bg"], b["d"]["W1"], b["d"]["b1"], b["d"]["W2"],
+                              b["d"]["b2"], b["y"], b["counts"], b["aux"], ws, topk_idx=idx, topk_w=w, stream=stream)
+        slot = region(moe.MOE_WS_SLOT, i32, T * k, 4)
+        outp = region(moe.MOE_WS_OUT, f32, R * D, 4)
+        for lst, flush in ((warm, False), (cold, True)):
+            if flush:
+                dst.copy_(src)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            moe.moe_combine(s, outp, slot, w, y2, stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            lst.append(1e3 * e0.elapsed_time(e1))
+    S = int(b["counts"].sum().item())
+    nbytes = S * D * 4 + T * D * 4 + T * k * 8
+    out = {"algorithmic_bytes": nbytes}
+    for name, lst in (("after_forward", warm), ("after_1GiB_stream", cold)):
+        us = float(np.median(lst))
+        out[name] = {"us": us, "GB/s": nbytes / (us * 1e-6) / 1e9, "frac_hbm": nbytes / (us * 1e-6) / PEAK_HBM}
+    del src, dst
+    return out
+
+
 def time_router_variant(moe, s, cfg, d, ws, stream):
     """The stable layer's router on the workload's gate logits: noisy top-1
     over the full softmax (moe_route_logits_ex, writing the noisy logits)
@@ -389,7 +437,9 @@ def time_router_variant(moe, s, cfg, d, ws, stream):
 def time_backward(moe, s, cfg, d, ws, stream, reps=5):
     """moe_layer_backward after one forward of the same batch (dy seeded
     N(0,1)); HIP events around each call.  FLOPs: five GEMMs of 2 S d d_ff
-    each (recompute, dh, dx_perm, dW1, dW2) plus the gate's two of 2 T d E."""
+    each (recompute, dh, dx_perm, dW1, dW2) plus the gate's two sums of
+    2 T k d (dWg and the gate's part of dx: k nonzero logit gradients per
+    token)."""
     import numpy as np
     import torch
     dev = d["x"].device
@@ -418,13 +468,16 @@ def time_backward(moe, s, cfg, d, ws, stream, reps=5):
     us = _median_us(lambda: moe.moe_layer_backward(s, d["x"], d["Wg"], d["W1"], d["b1"], d["W2"], dy, idx, w, slot,
                                                    offsets, xperm, outp, *g, bws, stream=stream), stream, reps)
     S = int(counts.cpu().numpy().sum())
-    flops = 10 * S * D * F + 4 * T * D * E
+    # five expert GEMMs over the kept rows; the gate's dWg and dx part are
+    # sums over the k selected experts of each token (the other logits have
+    # no gradient)
+    flops = 10 * S * D * F + 4 * T * cfg.k * D
     bf16 = cfg.dtype == "bf16"
     peak = PEAK_BF16 if bf16 else PEAK_FP32
     return {"ms": us / 1e3, "tflops": flops / (us * 1e-6) / 1e12, "flops": flops,
             "peak_tflops": peak / 1e12, "frac_peak": flops / (us * 1e-6) / peak,
-            "arith": ("expert GEMMs on bf16 MFMA (fp32 accumulate), gate GEMMs on fp32 vector ALUs" if bf16
-                      else "fp32 vector ALUs")}
+            "arith": ("expert GEMMs on bf16 MFMA (fp32 accumulate); gate gradients as fp32 sums over the k "
+                      "selected experts" if bf16 else "fp32 vector ALUs")}
 
 
 def prepare(moe, cfg, dev):
@@ -612,6 +665,9 @@ def main():
     out.update({k: v for k, v in summ.items() if k not in ("ms_per_step", "tokens_per_s", "roofline")})
     s, ws, y, counts, aux = b["s"], b["ws"], b["y"], b["counts"], b["aux"]
     out["heat_map"] = time_heat_map(moe, s, cfg, d, y, counts, aux, ws, stream)
+    # the combine's rate with its input out of the caches (the 256 MB MALL
+    # holds part of out_perm right after the forward)
+    out["combine_cold"] = time_combine_cold(moe, s, cfg, dict(b, d=d), stream)
     out["router_variant"] = time_router_variant(moe, s, cfg, d, ws, stream)
     if not args.no_backward:
         out["backward"] = time_backward(moe, s, cfg, d, ws, stream)

@@ -320,9 +320,11 @@ int moe_layer_forward(const moe_shape* s, const void* x, const float* Wg, const 
  * gradient w[t,j] dy[t] and da = dh GELU'(a) (2^-9 relative each, like h);
  * h is recomputed from x_perm, W1, b1 and rounded to bf16 as the forward
  * stores it, GELU and GELU' use the forward's erf approximation; db1 and
- * db2 are fp32 column sums of those bf16 values; the gate's GEMMs (dWg,
- * the gate's part of dx) run in fp32 on the vector ALUs (bf16 x widened
- * exactly).  ws: moe_backward_workspace_size bytes (its own workspace; the
+ * db2 are fp32 column sums of those bf16 values.  The gate's gradients
+ * (dWg, dbg and the gate's part of dx) are fp32 sums over the k selected
+ * experts of each token, the only logits with a gradient (bf16 x widened
+ * exactly): dWg[:, e] and dbg[e] sum over the tokens that selected e in
+ * token order, the gate's part of dx[t] sums over j in order.  ws: moe_backward_workspace_size bytes (its own workspace; the
  * forward's may be read through x_perm / out_perm, so the two must not
  * overlap). */
 size_t moe_backward_workspace_size(const moe_shape* s);

@@ -16,9 +16,10 @@
 //   4. dx_perm = da W1^T                   (rows of each expert);
 //   5. dW2[e] = h^T g, dW1[e] = x_perm^T da (sums over each expert's rows);
 //   6. db2[e], db1[e]: column sums of g and da over each expert's rows;
-//   7. gate: dl[t, idx_j] = w_j (dw_j - sum_i w_i dw_i) / tau, dWg = x^T dl,
-//      dbg = column sums of dl, dxg = dl Wg^T;
-//   8. dx[t] = sum_j dx_perm[slot[t,j]] + dxg[t].
+//   7. gate: dl[t, idx_j] = w_j (dw_j - sum_i w_i dw_i) / tau (zero at the
+//      other E - k logits), dWg = x^T dl and dbg = column sums of dl, each a
+//      sum over the tokens that selected the expert (grouped by expert);
+//   8. dx[t] = sum_j dx_perm[slot[t,j]] + sum_j dl[t, idx_j] Wg[:, idx_j].
 // Arithmetic.  fp32 layers: every GEMM in fp32 on the vector ALUs (one
 // tiled kernel, 64 x 64 outputs per workgroup, 4 x 4 per thread, K in steps
 // of 16 through LDS), GELU and GELU' from the device library's erff.  bf16
@@ -28,8 +29,9 @@
 // are rounded to bf16 (a 2^-9 relative rounding each, like h), h is
 // recomputed in bf16 and GELU / GELU' use the forward's erf approximation
 // (Abramowitz & Stegun 7.1.26); bias gradients are column sums of the bf16 g
-// and da in fp32; the gate's GEMMs stay on the fp32 vector-ALU kernel (bf16
-// x widened exactly when staged).  Three operand patterns:
+// and da in fp32.  The gate's gradients (both layer types) are fp32 sums of
+// the k nonzero terms per token (bf16 x widened exactly).  Three operand
+// patterns:
 //   NN: A rows of a segment, K-contiguous; B = W[e] [K][N]
 //   NT: A rows of a segment, K-contiguous; B = W[e] stored [N][K]
 //   TN: A and B both rows of a segment; K runs over the segment's rows
@@ -71,8 +73,7 @@ __device__ __forceinline__ float gelu_grad(float u) {
 }  // namespace
 
 // C[m][n] = sum_k A(m,k) B(k,n) for every item; see the header comment for
-// the operand patterns.  Row segments come from offsets[E+1] (or one segment
-// [0, M) when offsets is null).
+// the operand patterns.  Row segments come from offsets[E+1].
 template <int MODE, int EPI, typename TA, typename TB, typename TH>
 __global__ __launch_bounds__(BW_THREADS) void bw_gemm_kernel(BwGemmArgs g) {
     __shared__ __attribute__((aligned(16))) float As[BW_BK][BW_BM + BW_PAD];
@@ -95,42 +96,16 @@ __global__ __launch_bounds__(BW_THREADS) void bw_gemm_kernel(BwGemmArgs g) {
         m0 = (rest / ntn) * BW_BM;
         n0 = (rest % ntn) * BW_BN;
         mrows = min(BW_BM, g.M - m0);
-        if (g.offsets) {
-            kb = g.offsets[e];
-            kend = g.offsets[e + 1];
-        } else if (g.chunk > 0) {   // split K: output e is the partial sum over chunk e
-            kb = e * g.chunk;
-            kend = min(g.K, kb + g.chunk);
-        } else {
-            kb = 0;
-            kend = g.K;
-        }
+        kb = g.offsets[e];
+        kend = g.offsets[e + 1];
     } else {
-        int total_mt;
-        if (g.offsets) {
-            total_mt = build_mtile_prefix(g.offsets, g.E, BW_BM, mt_pre, scan_tmp);
-        } else {
-            total_mt = (g.M + BW_BM - 1) / BW_BM;
-        }
+        const int total_mt = build_mtile_prefix(g.offsets, g.E, BW_BM, mt_pre, scan_tmp);
         if ((int64_t)blockIdx.x >= (int64_t)total_mt * ntn) return;
-        int mt, nt, seg0, seg1;
-        if (g.offsets) {
-            const WorkItem wi = decode_item(mt_pre, g.E, ntn, blockIdx.x);
-            e = wi.e;
-            mt = wi.mt;
-            nt = wi.nt;
-            seg0 = g.offsets[e];
-            seg1 = g.offsets[e + 1];
-        } else {
-            e = 0;
-            mt = blockIdx.x % total_mt;
-            nt = blockIdx.x / total_mt;
-            seg0 = 0;
-            seg1 = g.M;
-        }
-        m0 = seg0 + mt * BW_BM;
-        mrows = min(BW_BM, seg1 - m0);
-        n0 = nt * BW_BN;
+        const WorkItem wi = decode_item(mt_pre, g.E, ntn, blockIdx.x);
+        e = wi.e;
+        m0 = g.offsets[e] + wi.mt * BW_BM;
+        mrows = min(BW_BM, g.offsets[e + 1] - m0);
+        n0 = wi.nt * BW_BN;
         kb = 0;
         kend = g.K;
     }
@@ -505,64 +480,221 @@ __global__ __launch_bounds__(256) void segment_colsum_bf16_kernel(const uint16_t
     }
 }
 
-// column sums of a [rows][N] fp32 matrix, one workgroup per column: fixed
-// per-thread row sets and a fixed reduction tree (bitwise repeatable)
-__global__ __launch_bounds__(256) void colsum_long_kernel(const float* __restrict__ src, int64_t rows, int N,
-                                                          float* __restrict__ out) {
-    __shared__ float part[256];
-    const int c = blockIdx.x;
-    float s = 0.0f;
-    for (int64_t r = threadIdx.x; r < rows; r += 256) s += src[r * N + c];
-    part[threadIdx.x] = s;
-    __syncthreads();
-    for (int w = 128; w > 0; w >>= 1) {
-        if (threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
-        __syncthreads();
-    }
-    if (threadIdx.x == 0) out[c] = part[0];
-}
+// ---- gate backward ----------------------------------------------------------
+// dl[t, e] is nonzero only at the k selected experts of token t, so both gate
+// GEMMs are sparse: dWg[:, e] = sum over the tokens that selected e of
+// dl[t, e] x[t], and dxg[t] = sum_j dl[t, j] Wg[:, idx_j].  The routed
+// (token, expert) pairs are grouped by expert with the dispatch's histogram and
+// scatter at unlimited capacity (every pair kept, token order within an
+// expert); dWg is then a gather-and-sum over each expert's rows and dxg is
+// folded into the assembly of dx.  Work and traffic scale with T k instead of
+// T E.
 
-// out[i] = sum over p of part[p][i], p in order
-__global__ __launch_bounds__(256) void sum_partials_kernel(const float* __restrict__ part, int np, int64_t n,
-                                                           float* __restrict__ out) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n) return;
-    float s = 0.0f;
-    for (int p = 0; p < np; ++p) s += part[(int64_t)p * n + i];
-    out[i] = s;
-}
-
-// gate softmax backward over the selected logits: one thread per token
+// gate softmax backward over the selected logits, one thread per token:
+// dl_j = w_j (dw_j - sum_i w_i dw_i) / tau (no other logit has a gradient);
+// dlsel[t, j] = dl_j and dlr[gslot[t, j]] = dl_j, beside the token's row in the
+// expert-grouped order
 __global__ __launch_bounds__(256) void gate_backward_kernel(int64_t T, int E, int k, float tau,
                                                             const int32_t* __restrict__ idx,
                                                             const float* __restrict__ w,
-                                                            const float* __restrict__ dw, float* __restrict__ dl) {
+                                                            const float* __restrict__ dw,
+                                                            const int32_t* __restrict__ gslot,
+                                                            float* __restrict__ dlsel, float* __restrict__ dlr) {
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= T) return;
     float s = 0.0f;
     for (int j = 0; j < k; ++j) s = fmaf(w[t * k + j], dw[t * k + j], s);
-    for (int e = 0; e < E; ++e) dl[t * E + e] = 0.0f;
     for (int j = 0; j < k; ++j) {
-        const int e = idx[t * k + j];
-        if ((unsigned)e < (unsigned)E) dl[t * E + e] = w[t * k + j] * (dw[t * k + j] - s) / tau;
+        const int64_t q = t * k + j;
+        const int e = idx[q];
+        const float v = (unsigned)e < (unsigned)E ? w[q] * (dw[q] - s) / tau : 0.0f;
+        dlsel[q] = v;
+        const int r = gslot[q];
+        if (r >= 0) dlr[r] = v;
     }
 }
 
-// dx[t] = sum_j dx_perm[slot[t,j]] (j order) + dxg[t]
-__global__ __launch_bounds__(256) void dispatch_backward_kernel(int64_t T, int d, int k,
+// wgt[e][c] = Wg[c][e], 64 x 64 tiles through LDS
+__global__ __launch_bounds__(256) void transpose_gate_kernel(const float* __restrict__ Wg, int d, int E,
+                                                             float* __restrict__ wgt) {
+    __shared__ float tile[64][65];
+    const int c0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
+    const int lo = threadIdx.x & 63, hi = threadIdx.x >> 6;
+    for (int cl = hi; cl < 64; cl += 4) {
+        const int c = c0 + cl, e = e0 + lo;
+        tile[cl][lo] = (c < d && e < E) ? Wg[(int64_t)c * E + e] : 0.0f;
+    }
+    __syncthreads();
+    for (int el = hi; el < 64; el += 4) {
+        const int e = e0 + el, c = c0 + lo;
+        if (c < d && e < E) wgt[(int64_t)e * d + c] = tile[lo][el];
+    }
+}
+
+template <typename TX>
+__device__ __forceinline__ void load8(const TX* p, float (&v)[8]);
+template <>
+__device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float (&v)[8]) {
+    const uint4 q = *reinterpret_cast<const uint4*>(p);
+    const uint32_t u[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(u[i] << 16);
+        v[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+    }
+}
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float (&v)[8]) {
+    const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+constexpr int GW_COLS = 512;   // columns of dWg per workgroup: 64 lanes x 8
+
+// partial sums of dWg over row chunks: item i (the mt-th chunk of
+// GATE_WGRAD_ROWS rows of expert e) writes part[i][c] = sum over its rows r of
+// dlr[r] x[gperm[r]][c], and its first column block also partb[i] = sum of
+// dlr[r].  Four row groups (rows r0 + g, r0 + g + 4, ...) are added in a fixed
+// order: bitwise repeatable.
+template <typename TX>
+__global__ __launch_bounds__(256) void gate_wgrad_kernel(const TX* __restrict__ x, const int32_t* __restrict__ gperm,
+                                                         const float* __restrict__ dlr,
+                                                         const int32_t* __restrict__ goff, int64_t T, int E,
+                                                         int d, float* __restrict__ part,
+                                                         float* __restrict__ partb) {
+    __shared__ int mt_pre[1025];
+    __shared__ int scan_tmp[32];
+    __shared__ float red[4][GW_COLS];
+    const int total = build_mtile_prefix(goff, E, GATE_WGRAD_ROWS, mt_pre, scan_tmp);
+    const int item = blockIdx.x;
+    if (item >= total) return;
+    const WorkItem wi = decode_item(mt_pre, E, 1, item);
+    const int r0 = goff[wi.e] + wi.mt * GATE_WGRAD_ROWS;
+    const int r1 = min(r0 + GATE_WGRAD_ROWS, goff[wi.e + 1]);
+    const int grp = threadIdx.x >> 6, cl = threadIdx.x & 63;
+    const int c0 = blockIdx.y * GW_COLS + cl * 8;
+    float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (c0 < d) {
+        // four rows in flight per lane: their token indices, then their x rows
+        for (int rb = r0 + grp; rb < r1; rb += 16) {
+            int64_t t[4];
+            float v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int r = rb + 4 * u;
+                t[u] = r < r1 ? gperm[r] : 0;
+                v[u] = r < r1 ? dlr[r] : 0.0f;
+            }
+            float xv[4][8];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                // (a token index out of range only follows repeated experts in topk_idx)
+                if (rb + 4 * u < r1 && (uint64_t)t[u] < (uint64_t)T) load8<TX>(x + t[u] * d + c0, xv[u]);
+                else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) xv[u][i] = 0.0f;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) s[i] = fmaf(v[u], xv[u][i], s[i]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) red[grp][cl * 8 + i] = s[i];
+    __syncthreads();
+    for (int c = threadIdx.x; c < GW_COLS; c += 256) {
+        const int col = blockIdx.y * GW_COLS + c;
+        if (col < d) part[(int64_t)item * d + col] = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
+    }
+    if (blockIdx.y == 0 && grp == 0) {
+        float b = 0.0f;
+        for (int r = r0 + cl; r < r1; r += 64) b += dlr[r];
+        b = wave_sum(b);
+        if (cl == 0) partb[item] = b;
+    }
+}
+
+// dWg[c][e] = sum of expert e's partial sums in chunk order, dbg[e] likewise.
+// A workgroup takes 64 columns x 16 experts and transposes through LDS, so
+// that the partial reads (along c) and the dWg writes (along e) are both
+// contiguous.  Experts without rows get zeros.
+constexpr int GR_E = 16;
+__global__ __launch_bounds__(256) void gate_wgrad_reduce_kernel(const float* __restrict__ part,
+                                                                const float* __restrict__ partb,
+                                                                const int32_t* __restrict__ goff, int E, int d,
+                                                                float* __restrict__ dWg, float* __restrict__ dbg) {
+    __shared__ int mt_pre[1025];
+    __shared__ int scan_tmp[32];
+    __shared__ float tile[64][GR_E + 1];
+    build_mtile_prefix(goff, E, GATE_WGRAD_ROWS, mt_pre, scan_tmp);
+    const int c0 = blockIdx.x * 64, e0 = blockIdx.y * GR_E;
+    {
+        const int lo = threadIdx.x & 63, hi = threadIdx.x >> 6;
+        for (int el = hi; el < GR_E; el += 4) {
+            const int e = e0 + el;
+            float s = 0.0f;
+            if (e < E && c0 + lo < d)
+                for (int it = mt_pre[e]; it < mt_pre[e + 1]; ++it) s += part[(int64_t)it * d + c0 + lo];
+            tile[lo][el] = s;
+        }
+    }
+    __syncthreads();
+    {
+        const int lo = threadIdx.x % GR_E, hi = threadIdx.x / GR_E;
+        for (int cl = hi; cl < 64; cl += 256 / GR_E) {
+            const int c = c0 + cl, e = e0 + lo;
+            if (c < d && e < E) dWg[(int64_t)c * E + e] = tile[cl][lo];
+        }
+    }
+    if (blockIdx.x == 0 && threadIdx.x < GR_E) {
+        const int e = e0 + threadIdx.x;
+        if (e < E) {
+            float s = 0.0f;
+            for (int it = mt_pre[e]; it < mt_pre[e + 1]; ++it) s += partb[it];
+            dbg[e] = s;
+        }
+    }
+}
+
+// dx[t] = sum_j dx_perm[slot[t,j]] over the kept slots, plus the gate's part
+// sum_j dl[t,j] Wg[:, idx_j] over the selected experts (both in j order);
+// one workgroup per token, 4 columns per thread
+__global__ __launch_bounds__(256) void dispatch_backward_kernel(int64_t T, int d, int k, int E,
                                                                 const float* __restrict__ dxp,
                                                                 const int32_t* __restrict__ slot,
-                                                                const float* __restrict__ dxg,
+                                                                const int32_t* __restrict__ idx,
+                                                                const float* __restrict__ dlsel,
+                                                                const float* __restrict__ wgt,
                                                                 float* __restrict__ dx) {
     const int64_t t = blockIdx.x;
-    for (int c = threadIdx.x; c < d; c += blockDim.x) {
-        float s = 0.0f;
+    for (int c = threadIdx.x * 4; c < d; c += blockDim.x * 4) {
+        float4 s = make_float4(0.f, 0.f, 0.f, 0.f), gs = make_float4(0.f, 0.f, 0.f, 0.f);
         for (int j = 0; j < k; ++j) {
             const int r = slot[t * k + j];
-            if (r >= 0) s += dxp[(int64_t)r * d + c];
+            if (r >= 0) {
+                const float4 v = *reinterpret_cast<const float4*>(dxp + (int64_t)r * d + c);
+                s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+            }
         }
-        dx[t * d + c] = s + dxg[t * d + c];
+        for (int j = 0; j < k; ++j) {
+            const int e = idx[t * k + j];
+            if ((unsigned)e < (unsigned)E) {
+                const float l = dlsel[t * k + j];
+                const float4 wv = *reinterpret_cast<const float4*>(wgt + (int64_t)e * d + c);
+                gs.x = fmaf(l, wv.x, gs.x); gs.y = fmaf(l, wv.y, gs.y);
+                gs.z = fmaf(l, wv.z, gs.z); gs.w = fmaf(l, wv.w, gs.w);
+            }
+        }
+        *reinterpret_cast<float4*>(dx + t * d + c) = make_float4(s.x + gs.x, s.y + gs.y, s.z + gs.z, s.w + gs.w);
     }
+}
+
+int64_t gate_wgrad_items(int64_t T, int k, int E) {
+    // each expert's last chunk may be partial: at most one extra item per expert
+    return (T * k + GATE_WGRAD_ROWS - 1) / GATE_WGRAD_ROWS + E;
 }
 
 // ---- host ------------------------------------------------------------------
@@ -572,8 +704,7 @@ static hipError_t bw_launch(const BwGemmArgs& g, int64_t max_rows, hipStream_t s
     const int ntn = (g.N + BW_BN - 1) / BW_BN;
     int64_t blocks;
     if (MODE == BW_TN) blocks = (int64_t)g.E * ((g.M + BW_BM - 1) / BW_BM) * ntn;
-    else if (g.offsets) blocks = ((max_rows + BW_BM - 1) / BW_BM + g.E) * ntn;   // bound; extra blocks exit
-    else blocks = (int64_t)((g.M + BW_BM - 1) / BW_BM) * ntn;
+    else blocks = ((max_rows + BW_BM - 1) / BW_BM + g.E) * ntn;   // bound; extra blocks exit
     if (blocks < 1) return hipSuccess;
     hipLaunchKernelGGL((bw_gemm_kernel<MODE, EPI, TA, TB, TH>), dim3((unsigned)blocks), dim3(BW_THREADS), 0, st, g);
     return hipGetLastError();
@@ -717,34 +848,33 @@ static hipError_t layer_backward_t(const BackwardArgs& b, hipStream_t st) {
                            reinterpret_cast<const TG*>(b.da), b.offsets, E, (int64_t)0, F, b.db1);
         BW_CHECK(hipGetLastError());
     }
-    // 7. gate (fp32 vector ALUs)
+    // 7. gate: group the routed (token, expert) pairs by expert, then
+    // dl, dWg and dbg over each expert's rows
+    DispatchArgs ga{};
+    ga.T = T; ga.E = E; ga.k = k;
+    ga.cap = T;   // a token holds an expert at most once: nothing is dropped
+    ga.max_rows = T * k;
+    ga.BT = b.BT; ga.nblk = b.nblk;
+    ga.idx = b.topk_idx; ga.blkhist = b.ghist; ga.offsets = b.goff; ga.perm = b.gperm; ga.slot = b.gslot;
+    BW_CHECK(launch_hist(ga, st));
+    BW_CHECK(launch_scatter(ga, st));
     hipLaunchKernelGGL(gate_backward_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, st, T, E, k, b.tau,
-                       b.topk_idx, b.topk_w, b.dw, b.dl);
+                       b.topk_idx, b.topk_w, b.dw, b.gslot, b.dlsel, b.dlr);
     BW_CHECK(hipGetLastError());
-    // dWg = x^T dl, split over token chunks (partials summed in chunk order)
-    BwGemmArgs g{};
-    g.A = b.x; g.lda = d;
-    g.B = b.dl; g.ldb = E;
-    g.E = b.gate_chunks; g.chunk = b.gate_chunk; g.M = d; g.N = E; g.K = (int)T;
-    g.C = b.dwg_part;
-    BW_CHECK((bw_launch<BW_TN, BWE_WGRAD, ET, float, float>(g, b.max_rows, st)));
-    {
-        const int64_t n = (int64_t)d * E;
-        hipLaunchKernelGGL(sum_partials_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, b.dwg_part,
-                           b.gate_chunks, n, b.dWg);
-        BW_CHECK(hipGetLastError());
-    }
-    hipLaunchKernelGGL(colsum_long_kernel, dim3((unsigned)E), dim3(256), 0, st, b.dl, T, E, b.dbg);
+    hipLaunchKernelGGL(transpose_gate_kernel, dim3((unsigned)((d + 63) / 64), (unsigned)((E + 63) / 64)), dim3(256), 0,
+                       st, b.Wg, d, E, b.wgt);
     BW_CHECK(hipGetLastError());
-    g = BwGemmArgs{};
-    g.A = b.dl; g.lda = E;
-    g.B = b.Wg; g.ldb = E;   // Wg [d][E] = [N][K]
-    g.E = 1; g.M = (int)T; g.K = E; g.N = d;
-    g.C = b.dxg;
-    BW_CHECK((bw_launch<BW_NT, BWE_STORE, float, float, float>(g, b.max_rows, st)));
-    // 8. dx
-    hipLaunchKernelGGL(dispatch_backward_kernel, dim3((unsigned)T), dim3(256), 0, st, T, d, k, b.dx_perm, b.slot,
-                       b.dxg, b.dx);
+    const dim3 wgrid((unsigned)gate_wgrad_items(T, k, E), (unsigned)((d + GW_COLS - 1) / GW_COLS));
+    hipLaunchKernelGGL(gate_wgrad_kernel<ET>, wgrid, dim3(256), 0, st, static_cast<const ET*>(b.x), b.gperm, b.dlr,
+                       b.goff, T, E, d, b.gpart, b.gpartb);
+    BW_CHECK(hipGetLastError());
+    const dim3 rgrid((unsigned)((d + 63) / 64), (unsigned)((E + GR_E - 1) / GR_E));
+    hipLaunchKernelGGL(gate_wgrad_reduce_kernel, rgrid, dim3(256), 0, st, b.gpart, b.gpartb, b.goff, E, d, b.dWg,
+                       b.dbg);
+    BW_CHECK(hipGetLastError());
+    // 8. dx, with the gate's part dl Wg^T
+    hipLaunchKernelGGL(dispatch_backward_kernel, dim3((unsigned)T), dim3(256), 0, st, T, d, k, E, b.dx_perm, b.slot,
+                       b.topk_idx, b.dlsel, b.wgt, b.dx);
     return hipGetLastError();
 }
 

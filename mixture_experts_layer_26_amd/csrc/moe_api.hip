@@ -502,8 +502,7 @@ int moe_aux_loss_ex(const moe_shape* s, int mode, const int32_t* load, float* au
 }
 
 struct BwLayout {
-    size_t g, h, hgrad, da, dx_perm, dw, dl, dxg, dwg_part, xperm, total;
-    int gate_chunks, gate_chunk;
+    size_t g, h, hgrad, da, dx_perm, dw, ghist, goff, gperm, gslot, dlsel, dlr, wgt, gpart, gpartb, xperm, total;
 };
 
 static BwLayout bw_layout(const Geo& g) {
@@ -520,13 +519,18 @@ static BwLayout bw_layout(const Geo& g) {
     L.hgrad = take(4 * R * g.dff);
     L.da = take(4 * R * g.dff);
     L.dx_perm = take(4 * R * g.d);
-    L.dw = take(4 * (size_t)(g.T * g.k));
-    L.dl = take(4 * (size_t)(g.T * g.E));
-    L.dxg = take(4 * (size_t)(g.T * g.d));
-    // dWg over token chunks of at least 512 rows, at most 64 chunks
-    L.gate_chunks = (int)std::min<int64_t>(64, (g.T + 511) / 512);
-    L.gate_chunk = (int)((g.T + L.gate_chunks - 1) / L.gate_chunks);
-    L.dwg_part = take(4 * (size_t)L.gate_chunks * g.d * g.E);
+    const size_t TK = (size_t)(g.T * g.k);
+    L.dw = take(4 * TK);
+    L.ghist = take(4 * (size_t)g.nblk * g.E);
+    L.goff = take(4 * (size_t)(g.E + 1));
+    L.gperm = take(4 * TK);
+    L.gslot = take(4 * TK);
+    L.dlsel = take(4 * TK);
+    L.dlr = take(4 * TK);
+    L.wgt = take(4 * (size_t)(g.E * g.d));
+    const size_t items = (size_t)gate_wgrad_items(g.T, (int)g.k, (int)g.E);
+    L.gpart = take(4 * items * g.d);
+    L.gpartb = take(4 * items);
     L.xperm = take((size_t)g.esz * R * g.d);   // the rows of x when the caller passes no x_perm
     L.total = p;
     return L;
@@ -587,11 +591,17 @@ int moe_layer_backward(const moe_shape* s, const void* x, const float* Wg, const
     b.da = at<float>(ws, L.da);
     b.dx_perm = at<float>(ws, L.dx_perm);
     b.dw = at<float>(ws, L.dw);
-    b.dl = at<float>(ws, L.dl);
-    b.dxg = at<float>(ws, L.dxg);
-    b.dwg_part = at<float>(ws, L.dwg_part);
-    b.gate_chunks = L.gate_chunks;
-    b.gate_chunk = L.gate_chunk;
+    b.BT = g.BT;
+    b.nblk = g.nblk;
+    b.ghist = at<int32_t>(ws, L.ghist);
+    b.goff = at<int32_t>(ws, L.goff);
+    b.gperm = at<int32_t>(ws, L.gperm);
+    b.gslot = at<int32_t>(ws, L.gslot);
+    b.dlsel = at<float>(ws, L.dlsel);
+    b.dlr = at<float>(ws, L.dlr);
+    b.wgt = at<float>(ws, L.wgt);
+    b.gpart = at<float>(ws, L.gpart);
+    b.gpartb = at<float>(ws, L.gpartb);
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (x_perm == nullptr)
         MOE_HIP(launch_gather_slots(g.T, (int)g.k, g.max_rows, g.d * g.esz, x, slot, at<void>(ws, L.xperm), st),

@@ -121,9 +121,8 @@ struct BwGemmArgs {
     const void* B;
     int64_t lda, ldb;
     int64_t b_estride;       // elements between experts' weight matrices (NN, NT)
-    const int32_t* offsets;  // row segments [E+1], or null: one segment (TN: E chunks of `chunk` rows)
+    const int32_t* offsets;  // row segments [E+1]
     int E, M, N, K;
-    int chunk;               // TN without offsets: rows per chunk (0: all K rows in one)
     const float* bias;       // NN recompute: b1 [E, N]
     void* C;                 // output
     float* C2;               // NN: GELU'(a) out; NT with GELU' product: GELU'(a) in
@@ -143,11 +142,21 @@ struct BackwardArgs {
     float* da;       // [max_rows, dff]
     float* dx_perm;  // [max_rows, d]
     float* dw;       // [T, k]
-    float* dl;       // [T, E]
-    float* dxg;      // [T, d]
-    float* dwg_part; // [gate_chunks, d, E] partial dWg over token chunks
-    int gate_chunks, gate_chunk;
+    // gate: the routed (token, expert) pairs grouped by expert (no capacity)
+    int BT, nblk;    // dispatch token block and block count
+    int32_t* ghist;  // [nblk, E]
+    int32_t* goff;   // [E+1]
+    int32_t* gperm;  // [T k] token of each grouped row
+    int32_t* gslot;  // [T k] grouped row of each (t, j)
+    float* dlsel;    // [T, k] gradient of the selected logits
+    float* dlr;      // [T k] the same per grouped row
+    float* wgt;      // [E, d] Wg transposed
+    float* gpart;    // [gate_wgrad_items, d] partial dWg over row chunks
+    float* gpartb;   // [gate_wgrad_items] partial dbg
 };
+// rows of one partial dWg sum; gate_wgrad_items bounds the number of chunks
+constexpr int GATE_WGRAD_ROWS = 128;
+int64_t gate_wgrad_items(int64_t T, int k, int E);
 hipError_t launch_layer_backward(const BackwardArgs& b, int dtype, hipStream_t st);
 
 // device properties (moe_api.hip)
