@@ -283,12 +283,25 @@ __global__ __launch_bounds__(256, MODE == BW_TN ? 4 : 1) void bw_mfma_kernel(BwG
 
     int e, m0, mrows, n0, kb, kend;
     if constexpr (MODE == BW_TN) {
+        // the dispatcher deals workgroups to the XCDs in turn (block b runs on
+        // XCD b % 8).  The longer output dimension is cut into 8 ranges and
+        // XCD x runs range x of every expert, expert by expert: its L2 holds
+        // 1/8 of the larger operand's rows and all of the smaller one's, and
+        // every XCD gets the same share of every expert.
         const int mtn = (g.M + BWM_BM - 1) / BWM_BM;
-        const int64_t item = blockIdx.x;
-        e = (int)(item / ((int64_t)mtn * ntn));
-        const int rest = (int)(item - (int64_t)e * mtn * ntn);
-        m0 = (rest / ntn) * BWM_BM;
-        n0 = (rest % ntn) * BWM_BN;
+        const int xcd = blockIdx.x % kXcds;
+        const int64_t i = blockIdx.x / kXcds;
+        const bool split_m = mtn >= ntn;
+        const int cut = split_m ? mtn : ntn, other = split_m ? ntn : mtn;
+        const int lo = xcd * cut / kXcds, span = (xcd + 1) * cut / kXcds - lo;
+        const int64_t per_e = (int64_t)span * other;
+        if (i >= (int64_t)g.E * per_e) return;
+        e = (int)(i / per_e);
+        const int rest = (int)(i - (int64_t)e * per_e);
+        const int mt = split_m ? lo + rest / ntn : rest / span;
+        const int nt = split_m ? rest % ntn : lo + rest % span;
+        m0 = mt * BWM_BM;
+        n0 = nt * BWM_BN;
         mrows = min(BWM_BM, g.M - m0);
         kb = g.offsets[e];
         kend = g.offsets[e + 1];
@@ -718,8 +731,10 @@ static hipError_t bw_launch(const BwGemmArgs& g, int64_t max_rows, hipStream_t s
 
 template <int MODE, int EPI>
 static hipError_t bwm_launch(const BwGemmArgs& g, int64_t max_rows, hipStream_t st) {
-    const int ntn = (g.N + BWM_BN - 1) / BWM_BN;
-    const int64_t blocks = (MODE == BW_TN) ? (int64_t)g.E * ((g.M + BWM_BM - 1) / BWM_BM) * ntn
+    const int ntn = (g.N + BWM_BN - 1) / BWM_BN, mtn = (g.M + BWM_BM - 1) / BWM_BM;
+    // TN: 8 XCD slots of the largest per-XCD share (see bw_mfma_kernel); extra blocks exit
+    const int cut = mtn >= ntn ? mtn : ntn, other = mtn >= ntn ? ntn : mtn;
+    const int64_t blocks = (MODE == BW_TN) ? (int64_t)kXcds * g.E * ((cut + kXcds - 1) / kXcds) * other
                                            : ((max_rows + BWM_BM - 1) / BWM_BM + g.E) * ntn;   // bound
     if (blocks < 1) return hipSuccess;
     hipLaunchKernelGGL((bw_mfma_kernel<MODE, EPI>), dim3((unsigned)blocks), dim3(256), 0, st, g);
