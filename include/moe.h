@@ -123,8 +123,8 @@ size_t moe_workspace_size(const moe_shape* s);
  * layers only: -1 for a bf16 layer, whose forward keeps x_perm only as
  * MOE_WS_XPT),
  * MOE_WS_XPT (bf16 layers: x_perm in the tile layout of MOE_WS_H below with
- * ceil(d/32) column tiles, the first GEMM's operand; padding rows and columns
- * d..32*ceil(d/32)-1 are zero),
+ * ceil(d/32) column tiles, the first GEMM's operand; padding rows are
+ * undefined, columns d..32*ceil(d/32)-1 of the kept rows are zero),
  * MOE_WS_H (h; fp32 layers: [max_rows,d_ff] row-major; bf16 layers: 16-row x
  * 32-column tiles over expert segments that start at multiples of 16 rows --
  * expert e's local row i is padded row p = P[e] + i with P[e] the sum of the

@@ -19,7 +19,7 @@
 //   gather  : x_perm[row] = x[perm[row]] with 16-byte vector copies, one
 //             wave per row; pads perm with -1 past the used rows (the fused
 //             bf16 forward uses gather_tiled_kernel instead: the same rows
-//             in the grouped GEMM's tile layout).
+//             in the grouped GEMM's tile layout, copied token by token).
 // gather_slots_kernel is the backward's copy of the rows, by slot.
 #include "ffn_sched.h"
 #include "moe_common.h"
@@ -163,41 +163,117 @@ __global__ __launch_bounds__(256) void gather_kernel(DispatchArgs a) {
     }
 }
 
-// The fused bf16 forward's copy: x_perm[row] = x[perm[row]] in the grouped
-// GEMM's 16-row x 32-column tile layout over expert segments padded to 16
-// rows (padded row p, column c at ((p / 16) KT + c / 32) 512 +
-// (p % 16) 32 + c % 32, KT = ceil(d / 32)).  In that layout one K-step of 16
-// rows of GEMM1's activation operand is one contiguous KiB: a global -> LDS
-// load of 64-byte row pieces moves half as many bytes per cycle as one of
-// contiguous KiBs.  Padding rows and columns d .. 32 KT - 1 are written as
-// zeros (the weight rows past d are zero, so the K tail must be finite).
-// One workgroup per 16-row block (one expert: segments are padded to 16),
-// in column spans of 1024: each wave reads whole rows (contiguous KiBs) into
-// an LDS block, then the span's tiles are written, one contiguous KiB per
-// wave instruction.  (The row-major x_perm is not written.)
+// The fused bf16 forward's copy of the kept rows into the grouped GEMM's
+// 16-row x 32-column tile layout over expert segments padded to 16 rows:
+// padded row p, column c at ((p / 16) KT + c / 32) 512 + (p % 16) 32 + c % 32,
+// KT = ceil(d / 32).  In that layout one K-step of 16 rows of GEMM1's
+// activation operand is one contiguous KiB: a global -> LDS load of 64-byte
+// row pieces moves half as many bytes per cycle as one of contiguous KiBs.
+// Columns d .. 32 KT - 1 are zeros (the weight rows past d read as zeros, so
+// the K tail must be finite).  Two ways, chosen in the kernel from the kept
+// row count S (offsets[E]):
+//   by token: a wave copies two tokens at a time, each row of x read once
+//     (1 KiB per load) and written to its k kept slots in 64-byte tile row
+//     pieces (4 lanes each), the slots' destinations found by k lanes at
+//     once; padding rows are not written (the grouped GEMM computes them but
+//     never stores their outputs);
+//   by block: a workgroup takes 16-row blocks, each wave a quarter of the
+//     block's tiles, each lane one 16-byte piece of row 16 pb + lane / 4 -- the gathered
+//     rows are read in 64-byte pieces and every tile is one contiguous KiB
+//     store; padding rows are written as zeros.
+// The token way reads T rows instead of the block way's S (with its
+// re-reads of a row's other copies, from cache) but scatters 64-byte writes,
+// which merge into whole lines while the written rows and x fit in the
+// last-level cache (256 MB).  It is taken when S >= 1.5 T, x is at least 12
+// MiB (below that the re-reads stay in cache) and (T + S) d 2 bytes <= 192
+// MiB.  Measured on MI355X (us, token / block way): 64 experts top-2 18.7 /
+// 21.8, 128 experts top-8 27.1 / 41.6, the 16-expert soft layer (k = 16,
+// x 8 MiB) 29.6 / 25.8, 16 experts top-2 8.4 / 9.0, 256 experts at T = 32768
+// 80.3 / 74.7, the literal Zipf bias (most slots dropped) 13.0 / 10.7.
+// Both pad perm with -1 past the used rows; the row-major x_perm is not
+// written.
+constexpr int GT_TOKENS = 16;   // tokens per workgroup pass (4 per wave)
+constexpr int GT_CPL = 8;       // 16-byte chunks per lane and token in one pass (d <= 4096)
+constexpr int GB_TILES = 8;     // tiles per wave in flight (block way)
+
+#ifndef MOE_GATHER_FORCE
+#define MOE_GATHER_FORCE 0   // 1: token way, 2: block way (timing builds only)
+#endif
+
 __global__ __launch_bounds__(256) void gather_tiled_kernel(DispatchArgs a, uint16_t* __restrict__ x_pt, int d) {
-    constexpr int SPAN = 1024;        // columns per pass
-    constexpr int LROW = SPAN + 32;   // LDS row stride: rows 64 bytes apart on the banks
     __shared__ int s_off[1025];
     __shared__ int s_poff[1025];
     __shared__ int scan_tmp[32];
-    __shared__ int s_src[16];
-    __shared__ __attribute__((aligned(16))) uint16_t buf[16 * LROW];
-    const int E = a.E;
+    const int E = a.E, k = a.k;
     for (int i = threadIdx.x; i <= E; i += blockDim.x) s_off[i] = a.offsets[i];
     __syncthreads();
     build_padded_offsets(s_off, E, s_poff, scan_tmp);   // ends with a barrier
     const int lane = threadIdx.x & (kWave - 1);
     const int wid = threadIdx.x / kWave;
     const int KT = (d + 31) >> 5;
-    const int dpad = KT * 32;
-    const int nblk16 = s_poff[E] >> 4;
+    const int nch = KT * 4;   // 16-byte chunks of a tiled row
+    const int d16 = d / 8;    // of them, the ones holding x (d is a multiple of 8)
     const uint4* __restrict__ x4 = static_cast<const uint4*>(a.x);
     uint4* __restrict__ t4 = reinterpret_cast<uint4*>(x_pt);
-    const int64_t d16 = d / 8;   // 16-byte chunks per row (d is a multiple of 8)
-    for (int pb = blockIdx.x; pb < nblk16; pb += gridDim.x) {
-        if (threadIdx.x < 16) {
-            const int p = (pb << 4) + threadIdx.x;
+    const int64_t S = s_off[E];
+    bool by_token = 2 * S >= 3 * a.T && a.T * (int64_t)d * 2 >= (int64_t(12) << 20) &&
+                    (a.T + S) * (int64_t)d * 2 <= (int64_t(192) << 20);
+    if (MOE_GATHER_FORCE) by_token = MOE_GATHER_FORCE == 1;
+    if (by_token) {
+        const int64_t step = (int64_t)gridDim.x * GT_TOKENS;
+        for (int64_t t0 = (int64_t)blockIdx.x * GT_TOKENS; t0 < a.T; t0 += step) {
+            // wave w copies tokens t0 + w + 4 u, two at a time
+            for (int u = 0; u < GT_TOKENS / 4; u += 2) {
+                const int64_t ta = t0 + wid + 4 * u, tb = ta + 4;
+                // lane j (< k) finds the tile row start of copy j of token a,
+                // lane 32 + j that of token b (k <= 32); -1: dropped
+                int64_t dst = -1;
+                {
+                    const int j = lane & 31;
+                    const int64_t t = lane < 32 ? ta : tb;
+                    if (j < k && t < a.T) {
+                        const int r = a.slot[t * k + j];
+                        const int e = a.idx[t * k + j];
+                        if (r >= 0 && (unsigned)e < (unsigned)E) {
+                            const int64_t p = (int64_t)r - s_off[e] + s_poff[e];
+                            dst = (p >> 4) * KT * 64 + (p & 15) * 4;
+                        }
+                    }
+                }
+                const int dlo = (int)(uint32_t)(uint64_t)dst, dhi = (int)(uint32_t)((uint64_t)dst >> 32);
+                for (int cb = 0; cb < nch; cb += kWave * GT_CPL) {
+                    uint4 va[GT_CPL], vb[GT_CPL];
+#pragma unroll
+                    for (int i = 0; i < GT_CPL; ++i) {
+                        const int c = cb + lane + kWave * i;
+                        va[i] = make_uint4(0u, 0u, 0u, 0u);
+                        vb[i] = make_uint4(0u, 0u, 0u, 0u);
+                        if (c < d16) {
+                            if (ta < a.T) va[i] = x4[ta * d16 + c];
+                            if (tb < a.T) vb[i] = x4[tb * d16 + c];
+                        }
+                    }
+                    for (int h = 0; h < 2; ++h) {
+                        for (int j = 0; j < k; ++j) {
+                            const int src = 32 * h + j;
+                            const int64_t base = (int64_t)(((uint64_t)(uint32_t)__shfl(dhi, src) << 32) |
+                                                           (uint32_t)__shfl(dlo, src));
+                            if (base < 0) continue;
+#pragma unroll
+                            for (int i = 0; i < GT_CPL; ++i) {
+                                const int c = cb + lane + kWave * i;
+                                if (c < nch) t4[base + (c >> 2) * 64 + (c & 3)] = h ? vb[i] : va[i];
+                            }
+                        }
+                    }
+                }
+            }
+        }
+    } else {
+        const int nblk16 = s_poff[E] >> 4;
+        for (int pb = blockIdx.x; pb < nblk16; pb += gridDim.x) {
+            // lane l: row p = 16 pb + l / 4 (its source token, or -1 for padding), piece l % 4
+            const int p = (pb << 4) + (lane >> 2);
             int lo = 0, hi = E;   // largest e with s_poff[e] <= p: the expert holding the block
             while (hi - lo > 1) {
                 const int mid = (lo + hi) >> 1;
@@ -205,45 +281,25 @@ __global__ __launch_bounds__(256) void gather_tiled_kernel(DispatchArgs a, uint1
                 else hi = mid;
             }
             const int local = p - s_poff[lo];
-            const int r = s_off[lo] + local;
-            const int src = local < s_off[lo + 1] - s_off[lo] ? a.perm[r] : -1;
-            const bool ok = (uint64_t)(int64_t)src < (uint64_t)a.T;
-            s_src[threadIdx.x] = ok ? src : -1;
-        }
-        __syncthreads();
-        for (int c0 = 0; c0 < dpad; c0 += SPAN) {
-            const int ncol = min(SPAN, dpad - c0);
-            // rows wid, wid + 4, ... : every load of the wave first, then the LDS stores
-            constexpr int CPL = SPAN / 8 / kWave;   // 16-byte chunks per lane and row
-            uint4 v[4][CPL];
+            const int src0 = local < s_off[lo + 1] - s_off[lo] ? a.perm[s_off[lo] + local] : -1;
+            const int64_t src = (uint64_t)(int64_t)src0 < (uint64_t)a.T ? src0 : -1;
+            const int piece = lane & 3;
+            // wave w: a contiguous quarter of the block's tiles, GB_TILES in flight
+            const int ct_end = (wid + 1) * KT / 4;
+            for (int ct0 = wid * KT / 4; ct0 < ct_end; ct0 += GB_TILES) {
+                uint4 v[GB_TILES];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int src = s_src[wid + 4 * q];
-#pragma unroll
-                for (int i = 0; i < CPL; ++i) {
-                    const int c = lane + kWave * i;
-                    const int64_t cg = c0 / 8 + c;   // chunk of the row
-                    v[q][i] = make_uint4(0u, 0u, 0u, 0u);
-                    if (c < ncol / 8 && src >= 0 && cg < d16) v[q][i] = x4[(int64_t)src * d16 + cg];
+                for (int i = 0; i < GB_TILES; ++i) {
+                    const int c = (ct0 + i) * 4 + piece;   // 16-byte chunk of the row
+                    v[i] = make_uint4(0u, 0u, 0u, 0u);
+                    if (ct0 + i < ct_end && src >= 0 && c < d16) v[i] = x4[src * d16 + c];
                 }
-            }
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-#pragma unroll
-                for (int i = 0; i < CPL; ++i) {
-                    const int c = lane + kWave * i;
-                    if (c < ncol / 8) *reinterpret_cast<uint4*>(&buf[(wid + 4 * q) * LROW + 8 * c]) = v[q][i];
-                }
-            __syncthreads();
-            const int row = lane >> 2, piece = lane & 3;
-            for (int t = wid; t < ncol / 32; t += 4) {
-                const uint4 v = *reinterpret_cast<const uint4*>(&buf[row * LROW + 32 * t + 8 * piece]);
-                t4[((int64_t)pb * KT + c0 / 32 + t) * 64 + row * 4 + piece] = v;
+                for (int i = 0; i < GB_TILES; ++i)
+                    if (ct0 + i < ct_end) t4[((int64_t)pb * KT + ct0 + i) * 64 + lane] = v[i];
             }
-            __syncthreads();
         }
     }
-    const int64_t S = s_off[E];
     const int64_t nthreads = (int64_t)gridDim.x * blockDim.x;
     for (int64_t r = S + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < a.max_rows; r += nthreads)
         a.perm[r] = -1;
@@ -251,7 +307,10 @@ __global__ __launch_bounds__(256) void gather_tiled_kernel(DispatchArgs a, uint1
 
 hipError_t launch_gather_tiled(const DispatchArgs& a, uint16_t* x_pt, int d, hipStream_t st) {
     if (a.E > 1024) return hipErrorInvalidValue;
-    int64_t blocks = h_tiled_rows(a.max_rows, a.E) / 16;   // one workgroup per 16-row block
+    // enough workgroups for either way: T / GT_TOKENS token groups or one per 16-row block
+    const int64_t by_block = h_tiled_rows(a.max_rows, a.E) / 16;
+    const int64_t by_token = (a.T + GT_TOKENS - 1) / GT_TOKENS;
+    int64_t blocks = by_block > by_token ? by_block : by_token;
     if (blocks > 65536) blocks = 65536;
     if (blocks < 1) blocks = 1;
     hipLaunchKernelGGL(gather_tiled_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a, x_pt, d);

@@ -68,6 +68,29 @@ def hot_cold_rows(counts, offsets, n=2):
     return np.concatenate([np.arange(offsets[e], offsets[e + 1], dtype=np.int64) for e in pick])
 
 
+def _check_tiled_copy(moe, s, wsh, cfg, dsp, x, name):
+    """The fused bf16 forward's tiled copy of x_perm (MOE_WS_XPT): kept row r
+    of expert e sits at padded row p = r - offsets[e] + P[e] (P: earlier
+    experts' counts rounded up to 16), element (p, c) at ((p / 16) KT + c / 32)
+    512 + (p % 16) 32 + c % 32; every kept row equals x[perm[r]] with zeros in
+    columns d .. 32 KT - 1 (padding rows are undefined).  Byte copy: bit-exact."""
+    d = cfg.d
+    KT = (d + 31) // 32
+    offs = dsp["offsets"].astype(np.int64)
+    S = int(offs[-1])
+    poff = np.concatenate([[0], np.cumsum((np.diff(offs) + 15) // 16 * 16)])
+    rows = np.arange(S, dtype=np.int64)
+    e = _expert_of_rows(dsp["offsets"], rows)
+    p = rows - offs[e] + poff[e]
+    nrow = int(poff[-1])
+    off = moe.moe_workspace_offset(s, moe.MOE_WS_XPT)
+    xpt = wsh[off:off + 2 * nrow * KT * 32].view(np.uint16).reshape(nrow // 16, KT, 16, 32)
+    got = xpt[p // 16, :, p % 16, :].reshape(S, KT * 32)
+    want = np.zeros((S, KT * 32), np.uint16)
+    want[:, :d] = x.view(np.uint16)[dsp["perm"][:S]]
+    assert np.array_equal(got, want), f"{name}: tiled x_perm rows"
+
+
 def _check_case(moe, orc, name):
     import torch
     cfg = get(name)
@@ -148,6 +171,8 @@ def _check_case(moe, orc, name):
     S = int(dsp["offsets"][-1])
     xp = H.to_host(xperm)
     assert np.array_equal(xp[:S], inp["x"].view(xp.dtype)[dsp["perm"][:S]]), f"{name}: x_perm rows"
+    if cfg.dtype == "bf16":
+        _check_tiled_copy(moe, s, wsh, cfg, dsp, inp["x"], name)
     # FFN rows: all of them for the small cases and FULL_Y; otherwise the
     # first and last row of every work item, the busiest and least busy
     # experts in full and the rows of the sampled tokens
