@@ -90,6 +90,10 @@ def parse():
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the measured copy and library-GEMM reference rates")
+    ap.add_argument("--forward-only", action="store_true",
+                    help="the timed layer forward of the one workload and nothing after it (for counter runs: "
+                         "no heat map, router variants, cold combine, backward, reference rates, oracle or "
+                         "other workloads)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -240,7 +244,7 @@ def write_traffic(fetch_csv: str, write_csv: str, workload: str, steps: int) -> 
             "kernel_source_hash": kernel_source_hash(),
             "commands": [
                 f"rocprofv3 --pmc {c} --output-format csv -d <dir> -o run -- python3 bench.py "
-                f"--config {workload} --steps {steps} --warmup 1 --no-cpu-baseline --copy-calib"
+                f"--config {workload} --steps {steps} --warmup 1 --forward-only --copy-calib"
                 for c in ("FETCH_SIZE", "WRITE_SIZE")],
         }
         with open(os.path.join(ROOT, "profiles", f"traffic_{stage}_{workload}.json"), "w") as f:
@@ -664,12 +668,14 @@ def main():
     }
     out.update({k: v for k, v in summ.items() if k not in ("ms_per_step", "tokens_per_s", "roofline")})
     s, ws, y, counts, aux = b["s"], b["ws"], b["y"], b["counts"], b["aux"]
-    out["heat_map"] = time_heat_map(moe, s, cfg, d, y, counts, aux, ws, stream)
-    # the combine's rate with its input out of the caches (the 256 MB MALL
-    # holds part of out_perm right after the forward)
-    out["combine_cold"] = time_combine_cold(moe, s, cfg, dict(b, d=d), stream)
-    out["router_variant"] = time_router_variant(moe, s, cfg, d, ws, stream)
-    if not args.no_backward:
+    fwd_only = args.forward_only
+    if not fwd_only:
+        out["heat_map"] = time_heat_map(moe, s, cfg, d, y, counts, aux, ws, stream)
+        # the combine's rate with its input out of the caches (the 256 MB MALL
+        # holds part of out_perm right after the forward)
+        out["combine_cold"] = time_combine_cold(moe, s, cfg, dict(b, d=d), stream)
+        out["router_variant"] = time_router_variant(moe, s, cfg, d, ws, stream)
+    if not args.no_backward and not fwd_only:
         out["backward"] = time_backward(moe, s, cfg, d, ws, stream)
     if args.copy_calib:
         src = torch.empty(COPY_CALIB_BYTES, dtype=torch.uint8, device=dev)
@@ -679,14 +685,14 @@ def main():
         torch.cuda.synchronize()
         out["copy_calib_bytes"] = COPY_CALIB_BYTES
     S, active = summ["kept_slots"], summ["active_experts"]
-    if not args.no_peaks and not args.copy_calib:
+    if not args.no_peaks and not args.copy_calib and not fwd_only:
         out["measured_peaks"] = measured_peaks(cfg, S, active, dev)
     del d, b, s, ws, y, counts, aux
     torch.cuda.empty_cache()
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not fwd_only:
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
     del inp
-    if not args.only:
+    if not args.only and not fwd_only:
         # every other workload (and the literal-Zipf reading of the headline):
         # the same timed forward, shorter runs, no backward or oracle
         out["configs"] = {}
