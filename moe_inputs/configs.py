@@ -125,6 +125,12 @@ _add(MoEConfig("e100_k5", T=1500, d=256, E=100, k=5, d_ff=200,
                gate_bias_std=0.3))
 _add(MoEConfig("e200_t33001", T=33001, d=64, E=200, k=2, d_ff=64,
                capacity_factor=1.1, bias_std=0.1, gate_bias_std=0.3))
+# the fused forward's token-by-token gather in two passes per row (d > 4096
+# columns: 576 chunks of 16 bytes against 512 per pass), with a K tail
+# (4608 = 144 x 32) and a gate over K = 4608
+_add(MoEConfig("wide_d", T=2048, d=4608, E=8, k=2, d_ff=64,
+               capacity_factor=0.0, bias_std=0.1, gate_bias_std=0.3,
+               note="x 18 MiB and S = 2T: the gather takes the token way"))
 _add(MoEConfig("cap_one", T=200, d=64, E=8, k=2, d_ff=64,
                capacity_factor=0.02, bias_std=0.1,
                note="capacity clips to 1 slot per expert"))

@@ -28,8 +28,8 @@ SMALL = ["tiny_fp32", "tiny_fp32_bias", "ragged_bf16", "ragged_fp32", "medium_bf
          "cap_one", "max_experts", "max_k", "soft_k_equals_e12", "k16_e40", "e100_k5",
          "e200_t33001"]
 FULL = ["bf16_e16", "multi_item", "skewed_e64", "skewed_e64_literal", "hybrid_e128", "large_e256", "dense_soft_e16",
-        "ragged_large", "ragged_large_even"]
-FULL_Y = {"bf16_e16", "multi_item"}   # the oracle over every token still takes seconds
+        "ragged_large", "ragged_large_even", "wide_d"]
+FULL_Y = {"bf16_e16", "multi_item", "wide_d"}   # the oracle over every token still takes seconds
 SAMPLE = 1024                  # tokens whose y is checked on the other full-size cases
 BLOCK = 64                     # row blocks of an expert segment whose first and last rows are checked
 
