@@ -693,10 +693,11 @@ def main():
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
     del inp
     if not args.only and not fwd_only:
-        # every other workload (and the literal-Zipf reading of the headline):
-        # the same timed forward, shorter runs, no backward or oracle
+        # every other workload (and the literal-Zipf reading of the headline,
+        # and the naive soft layer over all 128 experts): the same timed
+        # forward, shorter runs, no backward or oracle
         out["configs"] = {}
-        for name in WORKLOADS + ["skewed_e64_literal"]:
+        for name in WORKLOADS + ["skewed_e64_literal", "dense_soft_e128"]:
             if name == cfg.name:
                 continue
             c2 = get(name)

@@ -65,7 +65,7 @@
  *   writes nothing; moe_last_error() then holds a message for the calling
  *   thread.  A launch failure returns MOE_ERR_HIP.  Faults inside kernels
  *   surface at the caller's next synchronisation.
- * Shape limits: T >= 1, 1 <= E <= 1024, 1 <= k <= min(E, 32), d and d_ff
+ * Shape limits: T >= 1, 1 <= E <= 1024, 1 <= k <= E, d and d_ff
  *   positive multiples of 8 with d * d_ff <= 2^29, temperature > 0 and
  *   finite, T*k < 2^31.
  */
@@ -152,7 +152,12 @@ const char* moe_version(void);
  *    k <= 16 the gate runs on the matrix cores with Wg split exactly into
  *    three bf16 parts (kept in the workspace), which gives fp32-accurate
  *    products; otherwise on the vector ALUs in fp32.  Either way the same
- *    selection rule and weights.  ws: at least moe_workspace_size bytes. */
+ *    selection rule and weights.  For k <= 32 the selection runs inside the
+ *    gate kernel; for k > 32 (the soft layer over every expert, [EP] 2.2)
+ *    the gate writes the logits (to `logits`, else to the workspace) and a
+ *    second kernel selects by rank: expert e is the r-th choice with r the
+ *    number of experts whose logit is larger, or equal with a lower index.
+ *    ws: at least moe_workspace_size bytes. */
 int moe_route(const moe_shape* s, const void* x, const float* Wg, const float* bg,
               float* logits /* NULL ok */, int32_t* topk_idx, float* topk_w,
               void* ws, size_t ws_bytes, void* stream);
@@ -230,7 +235,8 @@ int moe_aux_loss(const moe_shape* s, const int32_t* counts, float* aux, void* st
  *       rounded to fp32 as the page's fp32 code does (0.1 on the page);
  *       `noise` holds the caller's standard-normal draws.
  *     noisy_logits (NULL ok, [T,E]) receives the routed values.
- *     Writes topk_idx [T,k] and topk_w [T,k]. */
+ *     Writes topk_idx [T,k] and topk_w [T,k].  k <= 32 (MOE_ERR_SHAPE
+ *     otherwise). */
 enum { MOE_ROUTER_TOPK = 0, MOE_ROUTER_TOP1_FULL = 1 };
 int moe_route_logits_ex(const moe_shape* s, int mode, const float* logits, const float* noise,
                         float noise_scale, int32_t* topk_idx, float* topk_w,

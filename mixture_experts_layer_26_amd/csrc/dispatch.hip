@@ -186,7 +186,7 @@ __global__ __launch_bounds__(256) void gather_kernel(DispatchArgs a) {
 // which merge into whole lines while the written rows and x fit in the
 // last-level cache (256 MB).  It is taken when S >= 1.5 T, x is at least 12
 // MiB (below that the re-reads stay in cache) and (T + S) d 2 bytes <= 192
-// MiB.  Measured on MI355X (us, token / block way): 64 experts top-2 18.7 /
+// MiB, with k <= 32.  Measured on MI355X (us, token / block way): 64 experts top-2 18.7 /
 // 21.8, 128 experts top-8 27.1 / 41.6, the 16-expert soft layer (k = 16,
 // x 8 MiB) 29.6 / 25.8, 16 experts top-2 8.4 / 9.0, 256 experts at T = 32768
 // 80.3 / 74.7, the literal Zipf bias (most slots dropped) 13.0 / 10.7.
@@ -216,7 +216,8 @@ __global__ __launch_bounds__(256) void gather_tiled_kernel(DispatchArgs a, uint1
     const uint4* __restrict__ x4 = static_cast<const uint4*>(a.x);
     uint4* __restrict__ t4 = reinterpret_cast<uint4*>(x_pt);
     const int64_t S = s_off[E];
-    bool by_token = 2 * S >= 3 * a.T && a.T * (int64_t)d * 2 >= (int64_t(12) << 20) &&
+    // (the token way holds a token's slots in 32 lanes: k <= 32)
+    bool by_token = k <= 32 && 2 * S >= 3 * a.T && a.T * (int64_t)d * 2 >= (int64_t(12) << 20) &&
                     (a.T + S) * (int64_t)d * 2 <= (int64_t(192) << 20);
     if (MOE_GATHER_FORCE) by_token = MOE_GATHER_FORCE == 1;
     if (by_token) {
@@ -327,14 +328,17 @@ __global__ __launch_bounds__(256) void gather_slots_kernel(int64_t T, int k, int
     const int64_t n16 = row_bytes / 16;
     const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x / kWave);
     for (int64_t t = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave; t < T; t += nwaves) {
-        const int my = lane < k ? slot[t * k + lane] : -1;
-        const uint64_t keep = __ballot((uint64_t)(int64_t)my < (uint64_t)max_rows);
         const uint4* s4 = reinterpret_cast<const uint4*>(static_cast<const char*>(x) + t * row_bytes);
-        for (uint64_t m = keep; m != 0; m &= m - 1) {
-            const int j = __ffsll((unsigned long long)m) - 1;
-            const int64_t row = __shfl(my, j, kWave);
-            uint4* d4 = reinterpret_cast<uint4*>(static_cast<char*>(x_perm) + row * row_bytes);
-            for (int64_t c = lane; c < n16; c += kWave) d4[c] = s4[c];
+        // the token's slots 64 at a time, one per lane
+        for (int j0 = 0; j0 < k; j0 += kWave) {
+            const int my = j0 + lane < k ? slot[t * k + j0 + lane] : -1;
+            const uint64_t keep = __ballot((uint64_t)(int64_t)my < (uint64_t)max_rows);
+            for (uint64_t m = keep; m != 0; m &= m - 1) {
+                const int j = __ffsll((unsigned long long)m) - 1;
+                const int64_t row = __shfl(my, j, kWave);
+                uint4* d4 = reinterpret_cast<uint4*>(static_cast<char*>(x_perm) + row * row_bytes);
+                for (int64_t c = lane; c < n16; c += kWave) d4[c] = s4[c];
+            }
         }
     }
 }

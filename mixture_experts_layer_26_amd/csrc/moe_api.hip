@@ -52,6 +52,7 @@ struct Geo {
     int esz;      // bytes per element of x / W / h
     int BT, nblk; // dispatch token blocks
     bool mfma_gate; // gate on matrix cores (bf16 x, E <= 256)
+    bool rank_route; // k above the register groups' 32: logits, then the selection by rank
 };
 
 // cap = min(T, ceil(cf * T * k / E)); cf <= 0: no limit.  cf*T*k is exact in
@@ -69,9 +70,8 @@ static int validate(const moe_shape* s, Geo* g) {
     if (s == nullptr) return fail(MOE_ERR_NULL, "shape is NULL");
     if (s->T < 1) return fail(MOE_ERR_SHAPE, "T must be >= 1 (got %lld)", (long long)s->T);
     if (s->E < 1 || s->E > 1024) return fail(MOE_ERR_SHAPE, "E must be in [1, 1024] (got %lld)", (long long)s->E);
-    if (s->k < 1 || s->k > s->E || s->k > 32)
-        return fail(MOE_ERR_SHAPE, "k must be in [1, min(E, 32)] (got k=%lld, E=%lld)", (long long)s->k,
-                    (long long)s->E);
+    if (s->k < 1 || s->k > s->E)
+        return fail(MOE_ERR_SHAPE, "k must be in [1, E] (got k=%lld, E=%lld)", (long long)s->k, (long long)s->E);
     if (s->d < 8 || s->d % 8 != 0) return fail(MOE_ERR_SHAPE, "d must be a positive multiple of 8 (got %lld)", (long long)s->d);
     if (s->d_ff < 8 || s->d_ff % 8 != 0)
         return fail(MOE_ERR_SHAPE, "d_ff must be a positive multiple of 8 (got %lld)", (long long)s->d_ff);
@@ -95,13 +95,15 @@ static int validate(const moe_shape* s, Geo* g) {
         g->esz = s->dtype == MOE_BF16 ? 2 : 4;
         g->BT = dispatch_block_tokens(s->T, (int)s->E, (int)s->k);
         g->nblk = (int)((s->T + g->BT - 1) / g->BT);
-        g->mfma_gate = route_mfma_supported(s->dtype, (int)s->E, (int)s->k);
+        g->rank_route = s->k > kRouteGroupMaxK;
+        // the selection by rank reads logits: the gate runs with no winners
+        g->mfma_gate = route_mfma_supported(s->dtype, (int)s->E, g->rank_route ? 0 : (int)s->k);
     }
     return MOE_OK;
 }
 
 struct WsLayout {
-    size_t gate, blkhist, offsets, idx, w, perm, slot, xperm, xpt, h, out, total;
+    size_t gate, logits, blkhist, offsets, idx, w, perm, slot, xperm, xpt, h, out, total;
 };
 
 static size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
@@ -115,6 +117,8 @@ static WsLayout ws_layout(const Geo& g) {
         return at;
     };
     L.gate = take(g.mfma_gate ? route_mfma_ws_bytes((int)g.d, (int)g.E) : 0);
+    // k > 32: the logits the selection by rank reads, when the caller keeps none
+    L.logits = take(g.rank_route ? sizeof(float) * (size_t)(g.T * g.E) : 0);
     L.blkhist = take(sizeof(int32_t) * (size_t)g.nblk * g.E);
     L.offsets = take(sizeof(int32_t) * (size_t)(g.E + 1));
     L.idx = take(sizeof(int32_t) * (size_t)(g.T * g.k));
@@ -203,6 +207,18 @@ static void stage_event(int stage, int after, hipStream_t st) {
 
 static hipError_t launch_route(const Geo& g, const moe_shape* s, const RouteArgs& ra, void* ws,
                                const WsLayout& L, hipStream_t st) {
+    if (g.rank_route) {
+        // the gate with no winners (logits only), then the selection by rank
+        RouteArgs lg = ra;
+        lg.k = 0;
+        if (lg.logits == nullptr) lg.logits = at<float>(ws, L.logits);
+        const hipError_t e = g.mfma_gate ? launch_route_mfma(lg, at<uint16_t>(ws, L.gate), device_cu_count(), st)
+                                         : launch_route_gate(lg, s->dtype, st);
+        if (e != hipSuccess) return e;
+        RouteArgs rk = ra;
+        rk.logits = lg.logits;
+        return launch_route_rank(rk, st);
+    }
     if (g.mfma_gate) return launch_route_mfma(ra, at<uint16_t>(ws, L.gate), device_cu_count(), st);
     return launch_route_gate(ra, s->dtype, st);
 }
@@ -331,7 +347,8 @@ int moe_route_logits(const moe_shape* s, const float* logits, int32_t* topk_idx,
     a.logits = const_cast<float*>(logits);
     a.idx = topk_idx;
     a.w = topk_w;
-    MOE_HIP(launch_route_logits(a, st), "route_logits kernel launch");
+    if (g.rank_route) MOE_HIP(launch_route_rank(a, st), "route_logits kernel launch");
+    else MOE_HIP(launch_route_logits(a, st), "route_logits kernel launch");
     return MOE_OK;
 }
 
@@ -472,6 +489,8 @@ int moe_route_logits_ex(const moe_shape* s, int mode, const float* logits, const
         return fail(MOE_ERR_SHAPE, "unknown router mode %d", mode);
     if (mode == MOE_ROUTER_TOP1_FULL && g.k != 1)
         return fail(MOE_ERR_SHAPE, "MOE_ROUTER_TOP1_FULL needs k = 1 (got k=%lld)", (long long)g.k);
+    if (g.k > kRouteGroupMaxK)
+        return fail(MOE_ERR_SHAPE, "the router variants take k <= %d (got k=%lld)", kRouteGroupMaxK, (long long)g.k);
     if (!std::isfinite(noise_scale)) return fail(MOE_ERR_SHAPE, "noise_scale must be finite");
     MOE_REQUIRE(logits);
     MOE_OPTIONAL(noise);

@@ -24,6 +24,10 @@ RouteArgs route_config(int64_t T, int d, int E, int k, float tau, int dtype, int
 size_t route_smem_bytes(const RouteArgs& a);
 hipError_t launch_route_gate(const RouteArgs& a, int dtype, hipStream_t st);
 hipError_t launch_route_logits(const RouteArgs& a, hipStream_t st);
+// top-k above the register groups' 32 winners: the selection by rank over
+// logits in global memory (any k <= E <= 1024)
+constexpr int kRouteGroupMaxK = 32;
+hipError_t launch_route_rank(const RouteArgs& a, hipStream_t st);
 hipError_t launch_route_variant(const RouteArgs& a, int mode, const float* noise, float scale, float* noisy,
                                 hipStream_t st);
 

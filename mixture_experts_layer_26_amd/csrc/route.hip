@@ -290,6 +290,59 @@ __global__ __launch_bounds__(256) void route_logits_topk_kernel(RouteArgs a) {
                            a.w + (active ? t : 0) * a.k);
 }
 
+// Top-k of any k <= E <= 1024 by rank, one wave per token: expert e's rank
+// is the number of experts that beat it (a larger logit, or an equal one at a
+// lower index), which is its place in the order the k rounds of selection
+// take; the experts of rank < k go to idx[t, rank] with weights
+// exp((l - l_top) / tau) over their sum (l_top: the largest logit, rank 0).
+// O(E^2) comparisons per token, the row read from LDS.  For k above the
+// register groups' 32, up to the soft MoE over every expert (k = E).
+constexpr int kRankMaxE = 1024;
+
+__global__ __launch_bounds__(64) void route_rank_kernel(RouteArgs a) {
+    __shared__ float row[kRankMaxE];
+    __shared__ int rank_s[kRankMaxE];
+    __shared__ float p_s[kRankMaxE];
+    const int64_t t = blockIdx.x;
+    const int E = a.E, k = a.k, lane = threadIdx.x;
+    const float* L = a.logits + t * E;
+    float top = -INFINITY;
+    for (int e = lane; e < E; e += kWave) {
+        row[e] = L[e];
+        top = fmaxf(top, L[e]);
+    }
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) top = fmaxf(top, __shfl_xor(top, off, kWave));
+    __syncthreads();
+    float z = 0.0f;
+    for (int e = lane; e < E; e += kWave) {
+        const float v = row[e];
+        int r = 0;
+        for (int e2 = 0; e2 < E; ++e2) {
+            const float u = row[e2];
+            r += (u > v || (u == v && e2 < e)) ? 1 : 0;
+        }
+        const float p = r < k ? expf((v - top) / a.tau) : 0.0f;
+        rank_s[e] = r;
+        p_s[e] = p;
+        z += p;
+    }
+    z = wave_sum(z);
+    for (int e = lane; e < E; e += kWave) {
+        const int r = rank_s[e];
+        if (r < k) {
+            a.idx[t * k + r] = e;
+            a.w[t * k + r] = p_s[e] / z;
+        }
+    }
+}
+
+hipError_t launch_route_rank(const RouteArgs& a, hipStream_t st) {
+    if (a.E > kRankMaxE) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(route_rank_kernel, dim3((unsigned)a.T), dim3(kWave), 0, st, a);
+    return hipGetLastError();
+}
+
 // fp32(l + fp32(scale * n)): two roundings, as two fp32 operations; the
 // pragma keeps the compiler from contracting them into one fused
 // multiply-add (one rounding), which routes differently at near-ties

@@ -150,6 +150,12 @@ _add(MoEConfig("ragged_large_even", T=32768, d=1000, E=8, k=2, d_ff=1976,
 _add(MoEConfig("dense_soft_e16", T=4096, d=1024, E=16, k=16, d_ff=4096,
                capacity_factor=0.0, temperature=0.2,
                note="k = E: the soft MoE of every expert, 4096 rows each"))
+# the page's naive soft MoE over all 128 experts ([EP] section 2.2): k = E =
+# 128 selects past the register router's 32 winners (the selection by rank),
+# 1024 rows per expert, 131072 rows through each grouped GEMM
+_add(MoEConfig("dense_soft_e128", T=1024, d=1024, E=128, k=128, d_ff=4096,
+               capacity_factor=0.0, temperature=0.2,
+               note="k = E = 128: every token through every expert"))
 
 # several grouped-GEMM work items per workgroup at long K, compared in full:
 # K = 1536 (48 K-steps) in both GEMMs, 6 column tiles of 256 and skewed
@@ -184,6 +190,13 @@ _add(MoEConfig("max_experts", T=2048, d=64, E=1024, k=4, d_ff=64,
                capacity_factor=1.0, bias_std=0.1))
 _add(MoEConfig("max_k", T=256, d=64, E=48, k=32, d_ff=64,
                capacity_factor=0.0, temperature=2.0, bias_std=0.1))
+# the selection by rank (k above 32): every expert of 64, compared in full;
+# 100 of 200 experts with a capacity limit (drops) and ragged d
+_add(MoEConfig("soft_k64_e64", T=384, d=128, E=64, k=64, d_ff=256,
+               capacity_factor=0.0, temperature=0.2, bias_std=0.1,
+               gate_bias_std=0.3))
+_add(MoEConfig("k100_e200", T=300, d=72, E=200, k=100, d_ff=96,
+               capacity_factor=0.9, temperature=0.7, bias_std=0.1))
 
 # The workload the throughput metric is quoted on (E=64, top-2, d=2048).
 HEADLINE = "skewed_e64"

@@ -82,16 +82,18 @@ def _header_enum(prefix):
     return {m.group(1): int(m.group(2)) for m in re.finditer(r"(%s\w+)\s*=\s*(\d+)" % prefix, src)}
 
 
-def test_workspace_regions_follow_the_header(moe):
+@pytest.mark.parametrize("E,k", [(12, 3), (48, 40)])
+def test_workspace_regions_follow_the_header(moe, E, k):
     """The MOE_WS_* values of the binding are the header's; every region of a
     bf16 and an fp32 layer is 256-byte aligned, the regions do not overlap and
     each holds its documented size (bf16: x_perm also in the tile layout over
     h_tiled_rows = 16 ceil((max_rows + 15 E) / 16) rows of 32 ceil(d / 32)
-    columns, and no row-major x_perm: its offset is -1)."""
+    columns, and no row-major x_perm: its offset is -1).  k = 40 takes the
+    selection by rank, whose logits also live in the workspace."""
     enum = _header_enum("MOE_WS_")
     assert enum and all(getattr(moe, k) == v for k, v in enum.items()), enum
     for dtype, esz in ((moe.MOE_BF16, 2), (moe.MOE_F32, 4)):
-        T, d, E, k, F = 3000, 200, 12, 3, 328
+        T, d, F = 3000, 200, 328
         s = moe.shape(T, d, E, k, F, 1.0, 1.0, 0.01, dtype)
         R = moe.moe_max_rows(s)
         ht = (R + 15 * E + 15) // 16 * 16
@@ -107,10 +109,12 @@ def test_workspace_regions_follow_the_header(moe):
         for (o1, n1), (o2, _) in zip(spans, spans[1:]):
             assert o1 + n1 <= o2
         assert spans[-1][0] + spans[-1][1] <= moe.moe_workspace_size(s)
+        if k > 32:
+            assert moe.moe_workspace_size(s) >= sum(n for _, n in spans) + 4 * T * E
 
 
 BAD_SHAPES = [
-    dict(T=0), dict(E=0), dict(E=1025), dict(k=0), dict(k=9, E=8), dict(k=33, E=64),
+    dict(T=0), dict(E=0), dict(E=1025), dict(k=0), dict(k=9, E=8), dict(k=65, E=64),
     dict(d=0), dict(d=12), dict(d_ff=20), dict(temperature=0.0), dict(temperature=float("inf")),
     dict(capacity_factor=float("nan")), dict(dtype=7),
 ]
@@ -173,6 +177,11 @@ def test_router_variant_and_loss_validation(moe):
     with pytest.raises(moe.MoEError) as ei:          # top-1 full softmax needs k = 1
         moe.moe_route_logits_ex(s2, moe.MOE_ROUTER_TOP1_FULL, p, p, p, stream=0)
     assert ei.value.status == 2 and "k = 1" in str(ei.value)
+    s33 = moe.shape(64, 64, 40, 33, 128)               # the variants keep k <= 32
+    assert moe.moe_workspace_size(s33) > 0
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_route_logits_ex(s33, moe.MOE_ROUTER_TOPK, p, p, p, stream=0)
+    assert ei.value.status == 2 and "k <= 32" in str(ei.value)
     s1 = moe.shape(64, 64, 8, 1, 128)
     with pytest.raises(moe.MoEError) as ei:
         moe.moe_route_logits_ex(s1, 7, p, p, p, stream=0)

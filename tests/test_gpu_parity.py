@@ -26,11 +26,12 @@ pytestmark = pytest.mark.gpu
 SMALL = ["tiny_fp32", "tiny_fp32_bias", "ragged_bf16", "ragged_fp32", "medium_bf16",
          "hybrid_small", "clustered_small", "single_token", "one_expert", "k_equals_e",
          "cap_one", "max_experts", "max_k", "soft_k_equals_e12", "k16_e40", "e100_k5",
-         "e200_t33001"]
+         "e200_t33001", "soft_k64_e64", "k100_e200"]
 FULL = ["bf16_e16", "multi_item", "skewed_e64", "skewed_e64_literal", "hybrid_e128", "large_e256", "dense_soft_e16",
-        "ragged_large", "ragged_large_even", "wide_d"]
+        "dense_soft_e128", "ragged_large", "ragged_large_even", "wide_d"]
 FULL_Y = {"bf16_e16", "multi_item", "wide_d"}   # the oracle over every token still takes seconds
 SAMPLE = 1024                  # tokens whose y is checked on the other full-size cases
+SAMPLE_OF = {"dense_soft_e128": 128}   # 128 experts per token: 16384 oracle rows
 BLOCK = 64                     # row blocks of an expert segment whose first and last rows are checked
 
 
@@ -138,7 +139,7 @@ def _check_case(moe, orc, name):
     aux_ref = orc.aux(dsp["counts"], T, k, cfg.aux_lambda)
     assert abs(float(H.to_host(aux)[0]) - aux_ref) <= H.TOL_AUX * abs(aux_ref) + 1e-12
 
-    toks = np.arange(T, dtype=np.int32) if (name in SMALL or name in FULL_Y) else H.sample_tokens(T, SAMPLE)
+    toks = np.arange(T, dtype=np.int32) if (name in SMALL or name in FULL_Y) else H.sample_tokens(T, SAMPLE_OF.get(name, SAMPLE))
     yref = orc.layer_tokens(toks, inp["x"], inp["W1"], inp["b1"], inp["W2"], inp["b2"], idx_ref,
                             dsp["slot"], w_ref)
     yh = H.to_host(y)
@@ -193,6 +194,21 @@ def _check_case(moe, orc, name):
     # the fused entry point runs the same kernels as the separate ones
     assert np.array_equal(H.to_host(y2), yh), f"{name}: fused and unfused y differ"
     assert abs(float(H.to_host(aux2)[0]) - aux_ref) <= H.TOL_AUX * abs(aux_ref) + 1e-12
+    if k > 32:
+        # the selection by rank on logits the workspace keeps (no caller buffer)
+        y3 = H.empty((T, d), f32)
+        idx3 = H.empty((T, k), i32)
+        w3 = H.empty((T, k), f32)
+        moe.moe_layer_forward(s, dv["x"], dv["Wg"], dv["bg"], dv["W1"], dv["b1"], dv["W2"], dv["b2"],
+                              y3, H.empty(E, i32), H.empty(1, f32), ws, topk_idx=idx3, topk_w=w3)
+        idx4 = H.empty((T, k), i32)
+        w4 = H.empty((T, k), f32)
+        moe.moe_route_logits(s, logits, idx4, w4)
+        torch.cuda.synchronize()
+        assert np.array_equal(H.to_host(y3), yh), f"{name}: y with the logits in the workspace"
+        for got, want, what in ((idx3, idx, "indices"), (w3, w, "weights"), (idx4, idx, "moe_route_logits indices"),
+                                (w4, w, "moe_route_logits weights")):
+            assert np.array_equal(H.to_host(got), H.to_host(want)), f"{name}: {what} (logits in the workspace)"
     H.log(f"[parity] {name}: ok  logits {gerr:.2e}  w {werr:.2e}  y {yerr:.2e}  S={S}/{T * k}  "
           f"rows checked {len(rows)}  tokens {len(toks)}")
     del dv, ws, xperm, out_perm
