@@ -10,7 +10,8 @@
 // the load-variance balance term) and coefficient of variation ([EP]
 // section 2.1).
 //
-// Integer work on T*k indices: every pair is one atomic increment.
+// Integer work on T*k indices: every pair is one atomic increment; a thread
+// takes one (token, position) at a time and pairs it with the later positions.
 //   * E <= 256: each workgroup keeps a private copy of H in LDS as packed
 //     16-bit counters (E*E/2 words, 128 KiB at E = 256) and of routed,
 //     counts its tokens with LDS atomics and adds its nonzero counters to
@@ -53,19 +54,22 @@ __global__ __launch_bounds__(kCoactThreads) void coact_kernel(const int32_t* __r
     const int64_t t0 = (int64_t)blockIdx.x * tok_per_blk;
     const int64_t t1 = min(T, t0 + tok_per_blk);
     const unsigned uE = (unsigned)E;
-    for (int64_t t = t0 + threadIdx.x; t < t1; t += blockDim.x) {
-        const int32_t* row = idx + t * k;
-        for (int a = 0; a < k; ++a) {
-            const int i = row[a];
-            if ((unsigned)i >= uE) continue;
-            atomicAdd(&lr[i], 1u);
-            for (int b = a + 1; b < k; ++b) {
-                const int j = row[b];
-                if ((unsigned)j >= uE) continue;
-                const int p = i * E + j;
-                if constexpr (kLds) atomicAdd(&lds[p >> 1], 1u << (16 * (p & 1)));
-                else atomicAdd(&H[p], 1);
-            }
+    // one (token, position a) per thread and turn: expert i = idx[t][a]
+    // against the experts at the later positions of the same token
+    const int64_t nq = t1 > t0 ? (t1 - t0) * k : 0;
+    for (int64_t q = threadIdx.x; q < nq; q += blockDim.x) {
+        const int64_t tq = q / k;
+        const int a = (int)(q - tq * k);
+        const int32_t* row = idx + (t0 + tq) * k;
+        const int i = row[a];
+        if ((unsigned)i >= uE) continue;
+        atomicAdd(&lr[i], 1u);
+        for (int b = a + 1; b < k; ++b) {
+            const int j = row[b];
+            if ((unsigned)j >= uE) continue;
+            const int p = i * E + j;
+            if constexpr (kLds) atomicAdd(&lds[p >> 1], 1u << (16 * (p & 1)));
+            else atomicAdd(&H[p], 1);
         }
     }
     __syncthreads();
@@ -156,9 +160,15 @@ hipError_t launch_coactivation(int64_t T, int k, int E, const int32_t* idx, int3
     hipLaunchKernelGGL(zero_i32_kernel, dim3((unsigned)zb), dim3(256), 0, st, H, nH, routed, (int64_t)E);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
 
-    // about one token per thread, at most one workgroup per CU, and few
-    // enough tokens per workgroup for the 16-bit counters
+    // about one token per thread, or about 64 pairs per thread where k is
+    // large (each thread takes one (token, position) at a time: with every
+    // token's whole list on one thread, 1024 tokens choosing all 128 experts
+    // ran 8128 pairs per thread on two CUs, 1.8 ms); at most one workgroup
+    // per CU, and few enough tokens per workgroup for the 16-bit counters
+    const int64_t pairs = T * (int64_t)k * (k - 1) / 2;
     int64_t blocks = (T + kCoactThreads - 1) / kCoactThreads;
+    const int64_t by_pairs = (pairs + 64 * kCoactThreads - 1) / (64 * kCoactThreads);
+    if (by_pairs > blocks) blocks = by_pairs;
     if (blocks > cus) blocks = cus;
     int64_t per = (T + blocks - 1) / blocks;
     if (per > kCoactMaxTokensPerBlock) {

@@ -75,8 +75,11 @@ def check(moe, orc, idx, E):
     (256, 8, 2),
     (1000, 257, 3),       # first E on global atomics
     (3001, 1000, 5),
-    (777, 1024, 32),      # largest E and k
+    (777, 1024, 32),      # largest E and k of the register router
     (70001, 200, 4),      # many workgroups, ragged tail
+    (1024, 128, 128),     # the soft layer over all 128 experts (every pair of every token)
+    (999, 200, 100),      # k > 32, ragged token blocks
+    (300, 1000, 600),     # k > 32 on global atomics
 ])
 def test_coactivation_parity(moe, orc, T, E, k):
     H.log(f"[coact] T={T} E={E} k={k}")
