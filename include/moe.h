@@ -323,9 +323,11 @@ int moe_layer_forward(const moe_shape* s, const void* x, const float* Wg, const 
  * Arithmetic.  fp32 layers: every GEMM in fp32 on the vector ALUs.  bf16
  * layers: the expert GEMMs run on bf16 matrix cores with fp32
  * accumulation, so their operands are rounded to bf16 -- the expert-output
- * gradient w[t,j] dy[t] and da = dh GELU'(a) (2^-9 relative each, like h);
- * h is recomputed from x_perm, W1, b1 and rounded to bf16 as the forward
- * stores it, GELU and GELU' use the forward's erf approximation; db1 and
+ * gradient w[t,j] dy[t] and da = dh GELU'(a) (2^-9 relative each, like h;
+ * GELU'(a) is kept in bf16 between the two GEMMs that make and use it, so
+ * da carries one more such rounding); h is recomputed from x_perm, W1, b1
+ * and rounded to bf16 as the forward stores it, GELU and GELU' use the
+ * forward's erf approximation; db1 and
  * db2 are fp32 column sums of those bf16 values.  The gate's gradients
  * (dWg, dbg and the gate's part of dx) are fp32 sums over the k selected
  * experts of each token, the only logits with a gradient (bf16 x widened

@@ -190,9 +190,9 @@ __global__ __launch_bounds__(BW_THREADS) void bw_gemm_kernel(BwGemmArgs g) {
                 if constexpr (EPI == BWE_HGRAD) {
                     v += g.bias[(int64_t)e * g.N + n];
                     st_elem<TH>(static_cast<TH*>(g.C), ci, gelu_erf(v));
-                    g.C2[ci] = gelu_grad(v);
+                    static_cast<float*>(g.C2)[ci] = gelu_grad(v);
                 } else if constexpr (EPI == BWE_DA) {
-                    static_cast<float*>(g.C)[ci] = v * g.C2[ci];
+                    static_cast<float*>(g.C)[ci] = v * static_cast<const float*>(g.C2)[ci];
                 } else {
                     static_cast<float*>(g.C)[ci] = v;
                 }
@@ -388,20 +388,23 @@ __global__ __launch_bounds__(256, MODE == BW_TN ? 4 : 1) void bw_mfma_kernel(BwG
                     v += bb;
                     // the erf of the forward's GELU (Abramowitz & Stegun 7.1.26),
                     // so h is rounded from the same function the forward stores
-                    uint16_t hb[4];
-                    f32x4_t gr;
+                    uint16_t hb[4], gb[4];
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         float hv, ga;
                         gelu_and_grad_as(v[q], hv, ga);
                         hb[q] = f32_to_bf16_bits(hv);
-                        gr[q] = ga;
+                        gb[q] = f32_to_bf16_bits(ga);
                     }
                     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(g.C) + ci) =
                         make_uint2(hb[0] | ((uint32_t)hb[1] << 16), hb[2] | ((uint32_t)hb[3] << 16));
-                    *reinterpret_cast<f32x4_t*>(g.C2 + ci) = gr;
+                    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(g.C2) + ci) =
+                        make_uint2(gb[0] | ((uint32_t)gb[1] << 16), gb[2] | ((uint32_t)gb[3] << 16));
                 } else if constexpr (EPI == BWE_DA) {
-                    const f32x4_t gr = *reinterpret_cast<const f32x4_t*>(g.C2 + ci);
+                    // GELU'(a) in bf16, as the recompute stored it
+                    const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(g.C2) + ci);
+                    const f32x4_t gr = {__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                                        __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
                     v *= gr;
                     const uint16_t d0 = f32_to_bf16_bits(v[0]), d1 = f32_to_bf16_bits(v[1]);
                     const uint16_t d2 = f32_to_bf16_bits(v[2]), d3 = f32_to_bf16_bits(v[3]);
@@ -758,7 +761,7 @@ static hipError_t ffn_backward_t(const BackwardArgs& b, hipStream_t st) {
         // large problems: the forward's pipelined GEMM with a GELU + GELU' epilogue
         GemmArgs p{};
         p.A = b.x_perm; p.B = b.W1; p.bias = b.b1; p.offsets = b.offsets;
-        p.E = E; p.K = d; p.N = F; p.out = b.h; p.out2 = b.hgrad;
+        p.E = E; p.K = d; p.N = F; p.out = b.h; p.out2 = static_cast<uint16_t*>(b.hgrad);
         hipError_t err = hipSuccess;
         if (launch_ffn_gemm_bf16_pipe(p, EPI_HGRAD, false, b.max_rows, st, &err)) BW_CHECK(err);
         else BW_CHECK((bwm_launch<BW_NN, BWE_HGRAD>(g, b.max_rows, st)));
@@ -775,7 +778,7 @@ static hipError_t ffn_backward_t(const BackwardArgs& b, hipStream_t st) {
         // large problems: the pipelined GEMM, W2[e] read K-contiguous, GELU' product epilogue
         GemmArgs p{};
         p.A = b.g; p.B = b.W2; p.bias = nullptr; p.offsets = b.offsets;
-        p.E = E; p.K = d; p.N = F; p.out = b.da; p.out2 = b.hgrad;
+        p.E = E; p.K = d; p.N = F; p.out = b.da; p.out2 = static_cast<uint16_t*>(b.hgrad);
         hipError_t err = hipSuccess;
         if (launch_ffn_gemm_bf16_pipe(p, EPI_DA, true, b.max_rows, st, &err)) BW_CHECK(err);
         else BW_CHECK((bwm_launch<BW_NT, BWE_DA>(g, b.max_rows, st)));

@@ -514,22 +514,26 @@ __device__ __forceinline__ void epilogue32(const GemmArgs& g, const Item<C>& it,
                         const f32x4_t b = *reinterpret_cast<const f32x4_t*>(&sbias[nl + 8 * j]);
                         const int e = 4 * (q + j);
                         if constexpr (EPI == EPI_DA) {
-                            // dh * GELU'(a): the factor read from out2 (a global load
-                            // here waits for the loads issued before it, in order)
+                            // dh * GELU'(a): the bf16 factor read from out2 (a global
+                            // load here waits for the loads issued before it, in order)
                             const int ng = it.n0 + nl + 8 * j;
                             f32x4_t gv = {0.f, 0.f, 0.f, 0.f};
-                            if (row_ok && ng < g.N) gv = *reinterpret_cast<const f32x4_t*>(g.out2 + row * g.N + ng);
+                            if (row_ok && ng < g.N) {
+                                const uint2 u = *reinterpret_cast<const uint2*>(g.out2 + row * g.N + ng);
+                                gv = f32x4_t{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                                             __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
+                            }
                             p[j][0] = pack_bf16x2(acc[mb][nb][e] * gv[0], acc[mb][nb][e + 1] * gv[1]);
                             p[j][1] = pack_bf16x2(acc[mb][nb][e + 2] * gv[2], acc[mb][nb][e + 3] * gv[3]);
                         } else if constexpr (EPI == EPI_HGRAD) {
-                            // GELU'(a) of this lane's quad straight to out2; h as below
+                            // GELU'(a) of this lane's quad straight to out2 in bf16; h as below
                             float hv[4], ga[4];
 #pragma unroll
                             for (int i = 0; i < 4; ++i) gelu_and_grad_as(acc[mb][nb][e + i] + b[i], hv[i], ga[i]);
-                            const f32x4_t gv = {ga[0], ga[1], ga[2], ga[3]};
                             const int ng = it.n0 + nl + 8 * j;
                             if (row_ok && ng < g.N)
-                                *reinterpret_cast<f32x4_t*>(g.out2 + row * g.N + ng) = gv;
+                                *reinterpret_cast<uint2*>(g.out2 + row * g.N + ng) =
+                                    make_uint2(pack_bf16x2(ga[0], ga[1]), pack_bf16x2(ga[2], ga[3]));
                             p[j][0] = pack_bf16x2(hv[0], hv[1]);
                             p[j][1] = pack_bf16x2(hv[2], hv[3]);
                         } else {

@@ -533,10 +533,12 @@ static BwLayout bw_layout(const Geo& g) {
         return at;
     };
     const size_t R = (size_t)g.max_rows;
-    L.g = take(4 * R * g.d);
+    // g, h, GELU'(a) and da in the layer dtype (bf16 operands of the
+    // matrix cores in bf16 layers)
+    L.g = take((size_t)g.esz * R * g.d);
     L.h = take((size_t)g.esz * R * g.dff);
-    L.hgrad = take(4 * R * g.dff);
-    L.da = take(4 * R * g.dff);
+    L.hgrad = take((size_t)g.esz * R * g.dff);
+    L.da = take((size_t)g.esz * R * g.dff);
     L.dx_perm = take(4 * R * g.d);
     const size_t TK = (size_t)(g.T * g.k);
     L.dw = take(4 * TK);
@@ -606,7 +608,7 @@ int moe_layer_backward(const moe_shape* s, const void* x, const float* Wg, const
     b.dx = dx; b.dWg = dWg; b.dbg = dbg; b.dW1 = dW1; b.db1 = db1; b.dW2 = dW2; b.db2 = db2;
     b.g = at<float>(ws, L.g);
     b.h = at<void>(ws, L.h);
-    b.hgrad = at<float>(ws, L.hgrad);
+    b.hgrad = at<void>(ws, L.hgrad);
     b.da = at<float>(ws, L.da);
     b.dx_perm = at<float>(ws, L.dx_perm);
     b.dw = at<float>(ws, L.dw);

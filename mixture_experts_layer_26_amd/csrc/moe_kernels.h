@@ -70,8 +70,8 @@ hipError_t launch_gather(const DispatchArgs& a, hipStream_t st);
 
 // ---- ffn_bf16.hip / ffn_fp32.hip ----------------------------------------
 // bf16 pipelined kernel only, for the backward (no bias, [rows, N] row-major):
-//   EPI_HGRAD: h = GELU(a) in bf16 to out and GELU'(a) in fp32 to out2;
-//   EPI_DA: (A B) * out2 (GELU'(a), read) in bf16 to out;
+//   EPI_HGRAD: h = GELU(a) and GELU'(a), both in bf16, to out and out2;
+//   EPI_DA: (A B) * out2 (GELU'(a) in bf16, read) in bf16 to out;
 //   EPI_WGRAD: out[e] [M, N] fp32 = A[seg(e)]^T B[seg(e)] with A [rows, M] and
 //   B [rows, N] row-major (the segments of offsets), zeros for idle experts
 enum { EPI_GELU_H = 0, EPI_STORE_F32 = 1, EPI_HGRAD = 2, EPI_DA = 3, EPI_WGRAD = 4 };
@@ -86,7 +86,7 @@ struct GemmArgs {
     // bf16 kernels: the EPI_GELU_H output and the EPI_STORE_F32 input A are h
     // in the tile layout of ffn_bf16.hip (h_tiled_rows rows); fp32 kernels:
     // row-major
-    float* out2;             // GELU'(a) [rows, N]: EPI_HGRAD output, EPI_DA input
+    uint16_t* out2;          // GELU'(a) [rows, N] bf16: EPI_HGRAD output, EPI_DA input
 };
 // rows of the h tile layout for max_rows packed rows over E experts
 inline int64_t h_tiled_rows(int64_t max_rows, int64_t E) { return ((max_rows + 15 * E + 15) / 16) * 16; }
@@ -129,7 +129,8 @@ struct BwGemmArgs {
     int E, M, N, K;
     const float* bias;       // NN recompute: b1 [E, N]
     void* C;                 // output
-    float* C2;               // NN: GELU'(a) out; NT with GELU' product: GELU'(a) in
+    void* C2;                // NN: GELU'(a) out; NT with GELU' product: GELU'(a) in
+                             // (bf16 in the matrix-core kernel, fp32 in the fp32 one)
 };
 struct BackwardArgs {
     int64_t T, max_rows;
@@ -140,10 +141,10 @@ struct BackwardArgs {
     const int32_t* offsets; const void* x_perm; const float* out_perm;
     float *dx, *dWg, *dbg, *dW1, *db1, *dW2, *db2;
     // workspace
-    float* g;        // [max_rows, d] expert-output gradients
+    float* g;        // [max_rows, d] expert-output gradients (layer dtype; bf16 read through casts)
     void* h;         // [max_rows, dff] recomputed GELU(a), layer dtype
-    float* hgrad;    // [max_rows, dff] GELU'(a)
-    float* da;       // [max_rows, dff]
+    void* hgrad;     // [max_rows, dff] GELU'(a), layer dtype
+    float* da;       // [max_rows, dff] (layer dtype)
     float* dx_perm;  // [max_rows, d]
     float* dw;       // [T, k]
     // gate: the routed (token, expert) pairs grouped by expert (no capacity)
