@@ -419,7 +419,22 @@ __global__ __launch_bounds__(256, MODE == BW_TN ? 4 : 1) void bw_mfma_kernel(BwG
 }
 
 // combine backward: per token, for each kept slot, dw = dy[t] . out[r] and
-// g[r] = w dy[t]; dropped slots get dw = 0
+// g[r] = w dy[t]; dropped slots get dw = 0.  A workgroup takes one token;
+// its four waves take the slots (G = 4 / min(k, 4) waves per slot for k < 4,
+// their partial dot products added in wave order), each lane four columns
+// at a time.
+template <typename TG>
+__device__ __forceinline__ void st4(TG* p, int64_t i, float4 v);
+template <>
+__device__ __forceinline__ void st4<float>(float* p, int64_t i, float4 v) {
+    *reinterpret_cast<float4*>(p + i) = v;
+}
+template <>
+__device__ __forceinline__ void st4<uint16_t>(uint16_t* p, int64_t i, float4 v) {
+    *reinterpret_cast<uint2*>(p + i) = make_uint2(f32_to_bf16_bits(v.x) | ((uint32_t)f32_to_bf16_bits(v.y) << 16),
+                                                  f32_to_bf16_bits(v.z) | ((uint32_t)f32_to_bf16_bits(v.w) << 16));
+}
+
 template <typename TG>
 __global__ __launch_bounds__(256) void combine_backward_kernel(int64_t T, int d, int k, const float* __restrict__ dy,
                                                                const float* __restrict__ out,
@@ -429,22 +444,38 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(int64_t T, int d,
     __shared__ float part[256 / kWave];
     const int64_t t = blockIdx.x;
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-    for (int j = 0; j < k; ++j) {
-        const int r = slot[t * k + j];
+    const int G = k == 1 ? 4 : k == 2 ? 2 : 1;   // waves per slot
+    const int NG = 4 / G;                         // slots in flight
+    const int sg = wid / G, sub = wid % G;
+    for (int j0 = 0; j0 < k; j0 += NG) {          // the same trip count in every wave
+        const int j = j0 + sg;
+        const int r = j < k ? slot[t * k + j] : -1;
         float s = 0.0f;
         if (r >= 0) {
             const float wt = w[t * k + j];
-            for (int c = threadIdx.x; c < d; c += blockDim.x) {
-                const float v = dy[t * d + c];
-                s = fmaf(v, out[(int64_t)r * d + c], s);
-                st_elem<TG>(g, (int64_t)r * d + c, wt * v);
+            for (int c = 4 * (sub * kWave + lane); c < d; c += 4 * kWave * G) {
+                const float4 v = *reinterpret_cast<const float4*>(dy + t * d + c);
+                const float4 o = *reinterpret_cast<const float4*>(out + (int64_t)r * d + c);
+                s = fmaf(v.x, o.x, s);
+                s = fmaf(v.y, o.y, s);
+                s = fmaf(v.z, o.z, s);
+                s = fmaf(v.w, o.w, s);
+                st4<TG>(g, (int64_t)r * d + c, make_float4(wt * v.x, wt * v.y, wt * v.z, wt * v.w));
             }
         }
         s = wave_sum(s);
-        if (lane == 0) part[wid] = s;
-        __syncthreads();
-        if (threadIdx.x == 0) dw[t * k + j] = (r >= 0) ? (part[0] + part[1] + part[2] + part[3]) : 0.0f;
-        __syncthreads();
+        if (G > 1) {
+            if (lane == 0) part[wid] = s;
+            __syncthreads();
+            if (sub == 0 && lane == 0 && j < k) {
+                float tot = part[sg * G];
+                for (int q = 1; q < G; ++q) tot += part[sg * G + q];
+                dw[t * k + j] = r >= 0 ? tot : 0.0f;
+            }
+            __syncthreads();
+        } else if (lane == 0 && j < k) {
+            dw[t * k + j] = r >= 0 ? s : 0.0f;
+        }
     }
 }
 
@@ -477,13 +508,25 @@ __global__ __launch_bounds__(256) void segment_colsum_bf16_kernel(const uint16_t
     const int r0 = offsets[e], r1 = offsets[e + 1];
     float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (c0 < N) {
-        for (int r = r0 + grp; r < r1; r += 4) {
-            const uint4 v = *reinterpret_cast<const uint4*>(src + (int64_t)r * N + c0);
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        // eight of the group's rows in flight, then added in row order (one
+        // load at a time waited on each: 94 us for the 64-expert layer's db1)
+        constexpr int U = 8;
+        for (int rb = r0 + grp; rb < r1; rb += 4 * U) {
+            uint4 v[U];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                s[2 * i] += __uint_as_float(w[i] << 16);
-                s[2 * i + 1] += __uint_as_float(w[i] & 0xffff0000u);
+            for (int u = 0; u < U; ++u) {
+                const int r = rb + 4 * u;
+                v[u] = r < r1 ? *reinterpret_cast<const uint4*>(src + (int64_t)r * N + c0) : make_uint4(0u, 0u, 0u, 0u);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (rb + 4 * u >= r1) break;
+                const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    s[2 * i] += __uint_as_float(w[i] << 16);
+                    s[2 * i + 1] += __uint_as_float(w[i] & 0xffff0000u);
+                }
             }
         }
     }
@@ -506,7 +549,8 @@ __global__ __launch_bounds__(256) void segment_colsum_bf16_kernel(const uint16_t
 // folded into the assembly of dx.  Work and traffic scale with T k instead of
 // T E.
 
-// gate softmax backward over the selected logits, one thread per token:
+// gate softmax backward over the selected logits, one wave per token (lane
+// j takes slots j, j + 64, ...):
 // dl_j = w_j (dw_j - sum_i w_i dw_i) / tau (no other logit has a gradient);
 // dlsel[t, j] = dl_j and dlr[gslot[t, j]] = dl_j, beside the token's row in the
 // expert-grouped order
@@ -516,11 +560,13 @@ __global__ __launch_bounds__(256) void gate_backward_kernel(int64_t T, int E, in
                                                             const float* __restrict__ dw,
                                                             const int32_t* __restrict__ gslot,
                                                             float* __restrict__ dlsel, float* __restrict__ dlr) {
-    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= T) return;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t t = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+    if (t >= T) return;   // wave-uniform
     float s = 0.0f;
-    for (int j = 0; j < k; ++j) s = fmaf(w[t * k + j], dw[t * k + j], s);
-    for (int j = 0; j < k; ++j) {
+    for (int j = lane; j < k; j += kWave) s = fmaf(w[t * k + j], dw[t * k + j], s);
+    s = wave_sum(s);
+    for (int j = lane; j < k; j += kWave) {
         const int64_t q = t * k + j;
         const int e = idx[q];
         const float v = (unsigned)e < (unsigned)E ? w[q] * (dw[q] - s) / tau : 0.0f;
@@ -876,7 +922,7 @@ static hipError_t layer_backward_t(const BackwardArgs& b, hipStream_t st) {
     ga.idx = b.topk_idx; ga.blkhist = b.ghist; ga.offsets = b.goff; ga.perm = b.gperm; ga.slot = b.gslot;
     BW_CHECK(launch_hist(ga, st));
     BW_CHECK(launch_scatter(ga, st));
-    hipLaunchKernelGGL(gate_backward_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, st, T, E, k, b.tau,
+    hipLaunchKernelGGL(gate_backward_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, T, E, k, b.tau,
                        b.topk_idx, b.topk_w, b.dw, b.gslot, b.dlsel, b.dlr);
     BW_CHECK(hipGetLastError());
     hipLaunchKernelGGL(transpose_gate_kernel, dim3((unsigned)((d + 63) / 64), (unsigned)((E + 63) / 64)), dim3(256), 0,
