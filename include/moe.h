@@ -149,7 +149,7 @@ const char* moe_version(void);
  *    the selected values; [PyTorchMoE] 3.2: the gate may carry a bias;
  *    [EP] 5.5: routing kept in fp32).  Writes topk_idx and topk_w; also the
  *    logits when `logits` is not NULL.  For bf16 x with E <= 256 and
- *    k <= 16 the gate runs on the matrix cores with Wg split exactly into
+ *    k <= 16 or k > 32 the gate runs on the matrix cores with Wg split exactly into
  *    three bf16 parts (kept in the workspace), which gives fp32-accurate
  *    products; otherwise on the vector ALUs in fp32.  Either way the same
  *    selection rule and weights.  For k <= 32 the selection runs inside the
