@@ -197,6 +197,12 @@ _add(MoEConfig("soft_k64_e64", T=384, d=128, E=64, k=64, d_ff=256,
                gate_bias_std=0.3))
 _add(MoEConfig("k100_e200", T=300, d=72, E=200, k=100, d_ff=96,
                capacity_factor=0.9, temperature=0.7, bias_std=0.1))
+# the selection by rank after the vector-ALU gate: an fp32 layer, and a bf16
+# layer of more than 256 experts
+_add(MoEConfig("k40_fp32", T=200, d=64, E=48, k=40, d_ff=64, dtype="fp32",
+               capacity_factor=1.2, temperature=0.5, bias_std=0.1))
+_add(MoEConfig("k50_e300", T=257, d=96, E=300, k=50, d_ff=64,
+               capacity_factor=0.0, temperature=1.0, bias_std=0.1, gate_bias_std=0.3))
 
 # The workload the throughput metric is quoted on (E=64, top-2, d=2048).
 HEADLINE = "skewed_e64"

@@ -26,7 +26,8 @@ pytestmark = pytest.mark.gpu
 
 TOL = {"fp32": 1e-4, "bf16": 1e-2}
 SMALL = ["tiny_fp32", "tiny_fp32_bias", "ragged_fp32", "ragged_bf16", "medium_bf16", "hybrid_small",
-         "clustered_small", "single_token", "one_expert", "k_equals_e", "cap_one", "soft_k64_e64", "k100_e200"]
+         "clustered_small", "single_token", "one_expert", "k_equals_e", "cap_one", "soft_k64_e64", "k100_e200", "k40_fp32",
+         "k50_e300"]
 # every gradient in full: several items per workgroup at K = 1536; long row
 # segments (the weight gradients' pipelined form); segments whose
 # weight-gradient operands span 2 GiB (past that form's 32-bit offsets)

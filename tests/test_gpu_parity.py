@@ -26,7 +26,7 @@ pytestmark = pytest.mark.gpu
 SMALL = ["tiny_fp32", "tiny_fp32_bias", "ragged_bf16", "ragged_fp32", "medium_bf16",
          "hybrid_small", "clustered_small", "single_token", "one_expert", "k_equals_e",
          "cap_one", "max_experts", "max_k", "soft_k_equals_e12", "k16_e40", "e100_k5",
-         "e200_t33001", "soft_k64_e64", "k100_e200"]
+         "e200_t33001", "soft_k64_e64", "k100_e200", "k40_fp32", "k50_e300"]
 FULL = ["bf16_e16", "multi_item", "skewed_e64", "skewed_e64_literal", "hybrid_e128", "large_e256", "dense_soft_e16",
         "dense_soft_e128", "ragged_large", "ragged_large_even", "wide_d"]
 FULL_Y = {"bf16_e16", "multi_item", "wide_d"}   # the oracle over every token still takes seconds
