@@ -10,7 +10,7 @@
 //
 // Launch sequence (moe_layer_backward):
 //   1. combine_backward: per kept slot, dw[t,j] = dy[t] . o[r] and the
-//      expert-output gradient g[r] = w[t,j] dy[t] (fp32, packed rows);
+//      expert-output gradient g[r] = w[t,j] dy[t] (packed rows);
 //   2. recompute per row a = x_perm W1 + b1 -> h = GELU(a), h' = GELU'(a);
 //   3. dh = g W2^T, da = dh * h'           (rows of each expert);
 //   4. dx_perm = da W1^T                   (rows of each expert);
@@ -26,8 +26,9 @@
 // layers: the expert GEMMs run on bf16 matrix cores with fp32 accumulation
 // (the forward's pipelined 256 x 256 kernel for large problems,
 // bw_mfma_kernel otherwise); their operands g = w dy and da = dh GELU'(a)
-// are rounded to bf16 (a 2^-9 relative rounding each, like h), h is
-// recomputed in bf16 and GELU / GELU' use the forward's erf approximation
+// are rounded to bf16 (a 2^-9 relative rounding each, like h; GELU'(a) is
+// kept in bf16 between the recompute and the dh GEMM), h is recomputed in
+// bf16 and GELU / GELU' use the forward's erf approximation
 // (Abramowitz & Stegun 7.1.26); bias gradients are column sums of the bf16 g
 // and da in fp32.  The gate's gradients (both layer types) are fp32 sums of
 // the k nonzero terms per token (bf16 x widened exactly).  Three operand
