@@ -23,7 +23,7 @@ def moe():
 @pytest.mark.parametrize("E,k,tau", [(8, 2, 1.0), (16, 3, 0.7), (64, 2, 1.0), (100, 7, 0.2),
                                      (128, 8, 0.2), (256, 2, 1.0), (1000, 5, 1.5), (1024, 32, 1.0),
                                      # k > 32: the selection by rank
-                                     (64, 64, 0.7), (200, 100, 0.2), (1024, 600, 1.0)])
+                                     (64, 64, 0.7), (200, 100, 0.2), (1024, 600, 1.0), (1024, 1024, 0.5)])
 def test_route_logits_ties(moe, orc, E, k, tau):
     import torch
     r = np.random.default_rng(E * 100 + k)
