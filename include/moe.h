@@ -157,7 +157,8 @@ const char* moe_version(void);
  *    the gate writes the logits (to `logits`, else to the workspace) and a
  *    second kernel selects by rank: expert e is the r-th choice with r the
  *    number of experts whose logit is larger, or equal with a lower index.
- *    ws: at least moe_workspace_size bytes. */
+ *    The logits must be finite (a NaN logit leaves the selection
+ *    unspecified).  ws: at least moe_workspace_size bytes. */
 int moe_route(const moe_shape* s, const void* x, const float* Wg, const float* bg,
               float* logits /* NULL ok */, int32_t* topk_idx, float* topk_w,
               void* ws, size_t ws_bytes, void* stream);
