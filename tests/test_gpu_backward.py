@@ -221,3 +221,46 @@ def test_backward_repeatable(moe):
     b, *_ = forward_backward(moe, cfg, inp, dy)
     for n in a:
         assert np.array_equal(a[n], b[n]), n
+
+
+def test_backward_soft_e128(moe, orc):
+    """The naive soft layer over all 128 experts (k = E = 128, 131072 rows,
+    1024 per expert) at full size: the weight and bias gradients of the first
+    and last expert over all their rows, dx of 8 seeded tokens (every one of
+    their 128 slots) and the gate sums.  The oracle takes each expert's
+    weights alone (an expert's gradients depend on its own rows only)."""
+    cfg = get("dense_soft_e128")
+    H.log(f"[backward-soft128] T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} d_ff={cfg.d_ff}")
+    inp = make_inputs(cfg)
+    dy = dy_of(cfg)
+    got, L, counts, offsets = forward_backward(moe, cfg, inp, dy)
+    tol = TOL[cfg.dtype]
+    idx, w = orc.route(L, cfg.k, cfg.temperature)
+    assert (counts == cfg.T).all()
+    slot = orc.dispatch(idx, cfg.E, orc.capacity(cfg.T, cfg.E, cfg.k, cfg.capacity_factor))["slot"]
+
+    def expert_rows(e, tt, jj):
+        sl = lambda a: np.ascontiguousarray(a[e:e + 1])
+        return orc.ffn_backward_rows(tt.astype(np.int32), np.zeros(len(tt), np.int32), w[tt, jj], inp["x"],
+                                     sl(inp["W1"]), sl(inp["b1"]), sl(inp["W2"]), sl(inp["b2"]), dy, 1)
+
+    for e in (0, cfg.E - 1):
+        tt, jj = np.nonzero(idx == e)
+        _, _, dW1, db1, dW2, db2 = expert_rows(e, tt, jj)
+        for n, ref in (("dW1", dW1), ("db1", db1), ("dW2", dW2), ("db2", db2)):
+            H.assert_close_norm(got[n][e], ref[0], tol, f"soft128 {n}[{e}]")
+    toks = H.sample_tokens(cfg.T, 8, seed=21)
+    dw = np.zeros((len(toks), cfg.k))
+    dx_ref = np.zeros((len(toks), cfg.d))
+    for e in range(cfg.E):
+        ti, jj = np.nonzero(idx[toks] == e)
+        dwr, dxp, *_ = expert_rows(e, toks[ti], jj)
+        dw[ti, jj] = dwr
+        np.add.at(dx_ref, ti, dxp)
+    assert (slot[toks] >= 0).all()
+    _, _, _, dxg = orc.route_backward(inp["x"][toks], inp["Wg"], idx[toks], w[toks], dw, cfg.temperature)
+    H.assert_close_norm(got["dx"][toks], dx_ref + dxg, tol, "soft128 dx (sampled)")
+    scale = np.abs(got["dbg"]).max() + 1e-30
+    assert abs(got["dbg"].sum()) <= 1e-3 * scale * np.sqrt(cfg.E)
+    rs = np.abs(got["dWg"].sum(axis=1)).max()
+    assert rs <= 1e-3 * (np.abs(got["dWg"]).max() + 1e-30) * np.sqrt(cfg.E)
