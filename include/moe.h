@@ -68,6 +68,11 @@
  * Shape limits: T >= 1, 1 <= E <= 1024, 1 <= k <= E, d and d_ff
  *   positive multiples of 8 with d * d_ff <= 2^29, temperature > 0 and
  *   finite, T*k < 2^31.
+ * Streams and graphs: the compute entry points only launch kernels on
+ *   `stream` (no allocation, no memset, no synchronisation), so after one
+ *   eager call with a shape (which caches device attributes) a call can be
+ *   captured into a HIP graph and replayed; every replay overwrites the
+ *   outputs and needs the same workspace contents as an eager call (none).
  */
 #ifndef MOE_H
 #define MOE_H
