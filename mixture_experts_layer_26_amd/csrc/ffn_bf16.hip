@@ -203,6 +203,7 @@ struct Loader {
     int E, K, N, M, ntn, mtn, wid;
     int a_rl, a_ps, b_rl, b_pc;   // BKC: b_rl, b_pc as a_rl, a_ps
     int a_kt;            // A in the tile layout: 32-column tiles per 16-row block
+    bool tail = false;   // items are the experts' tails (mt_pre counts them; see the split kernel)
     static constexpr int B_ROWS_PER_DMA = 512 / C::BN;
 
     __device__ __forceinline__ Loader(const GemmArgs& g, const int* off, const int* pre, const int* poff, int ntn_,
@@ -241,12 +242,14 @@ struct Loader {
         }
         const WorkItem wi = decode_item(mt_pre, E, ntn, item);
         const int e = __builtin_amdgcn_readfirstlane(wi.e);
-        const int m0 = __builtin_amdgcn_readfirstlane(s_off[e] + wi.mt * C::BM);
+        // a tail item starts after the expert's whole 256-row blocks
+        const int r0 = tail ? (s_off[e + 1] - s_off[e]) & ~255 : wi.mt * C::BM;
+        const int m0 = __builtin_amdgcn_readfirstlane(s_off[e] + r0);
         it.e = e;
         it.m0 = m0;
         it.mrows = __builtin_amdgcn_readfirstlane(min(C::BM, s_off[e + 1] - m0));
         it.n0 = __builtin_amdgcn_readfirstlane(wi.nt * C::BN);
-        it.pm0 = __builtin_amdgcn_readfirstlane(s_poff[e] + wi.mt * C::BM);
+        it.pm0 = __builtin_amdgcn_readfirstlane(s_poff[e] + r0);
         it.nk = (K + BK - 1) / BK;
         it.nks = it.nk + (it.nk & 1);
     }
@@ -673,41 +676,14 @@ __global__ __launch_bounds__(C::NT) void ffn_gemm_bf16_kernel(GemmArgs g) {
 // load in flight.  The load cursor runs NS steps ahead; an item has two
 // steps or more, so it is at most ceil(NS / 2) items ahead and NS bias slots
 // (NS >= 3) never overwrite one still in use.
-//
-// WPE: waves per SIMD the kernel is built for (register budget 512 / WPE).
-// AT: A in the h tile layout; BKC: B stored K-contiguous ([E, N, K]); TN:
-// the weight-gradient form of Loader (K-steps per item vary; items without
-// any K-step skip the ring and store zeros).
-template <class C, int NS, int EMAX, int WPE, int EPI, bool AT, bool BKC, bool TN>
-__global__ __launch_bounds__(C::NT, WPE) void ffn_gemm_bf16_pipe_kernel(GemmArgs g) {
-    static_assert(C::MF == 32 && C::BN == 256, "256-column tiles on 32x32x16 MFMAs");
-    static_assert(NS >= 3 && NS <= 4, "ring depth");
-    __shared__ __attribute__((aligned(1024))) uint16_t sa[NS][C::BM * BK];
-    __shared__ __attribute__((aligned(1024))) uint16_t sb[NS][BK * C::BN];
-    __shared__ int mt_pre[EMAX + 1];
-    __shared__ int s_off[EMAX + 1];
-    __shared__ int s_poff[EMAX + 1];
-    __shared__ int scan_tmp[32];
-    __shared__ __attribute__((aligned(16))) float s_bias[NS][C::BN];   // by item number mod NS
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform: scalar branches
-    const int wm = wid / C::WN, wn = wid % C::WN;
-    const int E = g.E, N = g.N;
-    const int ntn = (N + C::BN - 1) / C::BN;
 
-    for (int i = tid; i <= E; i += C::NT) s_off[i] = g.offsets[i];
-    int64_t total;
-    if constexpr (TN) {
-        __syncthreads();
-        total = (int64_t)E * ((g.M + C::BM - 1) / C::BM) * ntn;
-    } else {
-        total = (int64_t)build_mtile_prefix(g.offsets, E, C::BM, mt_pre, scan_tmp) * ntn;   // ends with a barrier
-        build_padded_offsets(s_off, E, s_poff, scan_tmp);
-    }
-    const ItemRange range = xcd_item_range(total);
-    if (range.first >= range.end) return;
-    const Loader<C, AT, BKC, TN> ld(g, s_off, mt_pre, s_poff, ntn, wid, lane);
+// The pipelined K-loop over one workgroup's items `range`; the ring, the
+// bias slots and the loader's LDS tables come from the caller.
+template <class C, int NS, int EPI, bool AT, bool BKC, bool TN>
+__device__ __forceinline__ void pipe_run(const GemmArgs& g, const Loader<C, AT, BKC, TN>& ld, const ItemRange range,
+                                         uint16_t (*sa)[C::BM * BK], uint16_t (*sb)[BK * C::BN],
+                                         float (*s_bias)[C::BN], int wid, int lane) {
+    const int wm = wid / C::WN, wn = wid % C::WN;
     constexpr int PER = C::A_DMA + C::B_DMA;
     constexpr bool kBias = EPI != EPI_WGRAD;
 
@@ -797,6 +773,117 @@ __global__ __launch_bounds__(C::NT, WPE) void ffn_gemm_bf16_pipe_kernel(GemmArgs
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// WPE: waves per SIMD the kernel is built for (register budget 512 / WPE).
+// AT: A in the h tile layout; BKC: B stored K-contiguous ([E, N, K]); TN:
+// the weight-gradient form of Loader (K-steps per item vary; items without
+// any K-step skip the ring and store zeros).
+template <class C, int NS, int EMAX, int WPE, int EPI, bool AT, bool BKC, bool TN>
+__global__ __launch_bounds__(C::NT, WPE) void ffn_gemm_bf16_pipe_kernel(GemmArgs g) {
+    static_assert(C::MF == 32 && C::BN == 256, "256-column tiles on 32x32x16 MFMAs");
+    static_assert(NS >= 3 && NS <= 4, "ring depth");
+    __shared__ __attribute__((aligned(1024))) uint16_t sa[NS][C::BM * BK];
+    __shared__ __attribute__((aligned(1024))) uint16_t sb[NS][BK * C::BN];
+    __shared__ int mt_pre[EMAX + 1];
+    __shared__ int s_off[EMAX + 1];
+    __shared__ int s_poff[EMAX + 1];
+    __shared__ int scan_tmp[32];
+    __shared__ __attribute__((aligned(16))) float s_bias[NS][C::BN];   // by item number mod NS
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform: scalar branches
+    const int E = g.E, N = g.N;
+    const int ntn = (N + C::BN - 1) / C::BN;
+
+    for (int i = tid; i <= E; i += C::NT) s_off[i] = g.offsets[i];
+    int64_t total;
+    if constexpr (TN) {
+        __syncthreads();
+        total = (int64_t)E * ((g.M + C::BM - 1) / C::BM) * ntn;
+    } else {
+        total = (int64_t)build_mtile_prefix(g.offsets, E, C::BM, mt_pre, scan_tmp) * ntn;   // ends with a barrier
+        build_padded_offsets(s_off, E, s_poff, scan_tmp);
+    }
+    const ItemRange range = xcd_item_range(total);
+    if (range.first >= range.end) return;
+    const Loader<C, AT, BKC, TN> ld(g, s_off, mt_pre, s_poff, ntn, wid, lane);
+    pipe_run<C, NS, EPI, AT, BKC, TN>(g, ld, range, sa, sb, s_bias, wid, lane);
+}
+
+#ifndef MOE_TAIL_WEIGHT
+#define MOE_TAIL_WEIGHT 75   // a tail item's work in hundredths of a full item's
+#endif
+#ifndef MOE_TILE_TAIL
+#define MOE_TILE_TAIL 128, 256, 2, 4, 32
+#endif
+using TileTail = TileCfg<MOE_TILE_TAIL>;
+
+// The first grouped GEMM with the experts' short tails on 128-row tiles.
+// An expert of r rows has floor(r / 256) whole 256-row blocks; a remainder
+// above 128 rows is one more 256-row item, one of 1..128 rows a tail item
+// on a 128 x 256 tile (a 128-row tile costs about two thirds of a 256-row
+// one on whole launches).  Tails and full items run at the same time in one
+// launch, on workgroups of two roles: the last nB of each die's workgroups
+// take the tail items, the others the full ones, nB in proportion to each
+// role's work (tail items weighted 0.75: measured best of 0.65, 0.75 and
+// 0.9 on the 64-expert workloads); both lists
+// run expert by expert, so an expert's tail and full items share its
+// weight tiles in the die's L2.  Every workgroup derives nB from the same
+// offsets.  Each role runs the same pipeline as ffn_gemm_bf16_pipe_kernel
+// with its own tile shape over one LDS ring.
+template <int NS, int EPI, bool AT>
+__global__ __launch_bounds__(TilePipe::NT, 2) void ffn_gemm_bf16_split_kernel(GemmArgs g) {
+    using CA = TilePipe;
+    using CB = TileTail;
+    static_assert(CA::NT == CB::NT && CA::BN == 256 && CB::BN == 256 && CA::BM == 256 && CB::BM == 128,
+                  "256- and 128-row tiles of 256 columns on the same waves");
+    static_assert(NS >= 3 && NS <= 4, "ring depth");
+    constexpr int RING_A = NS * (CA::BM * BK + BK * CA::BN), RING_B = NS * (CB::BM * BK + BK * CB::BN);
+    __shared__ __attribute__((aligned(1024))) uint16_t ring[RING_A > RING_B ? RING_A : RING_B];
+    __shared__ int mt_full[1025], mt_tail[1025], s_off[1025], s_poff[1025], scan_tmp[32];
+    __shared__ __attribute__((aligned(16))) float s_bias[NS][CA::BN];
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int E = g.E;
+    const int ntn = (g.N + CA::BN - 1) / CA::BN;
+    for (int i = tid; i <= E; i += CA::NT) s_off[i] = g.offsets[i];
+    const int64_t full = (int64_t)build_mtile_prefix(g.offsets, E, 256, mt_full, scan_tmp, kTilesFull) * ntn;
+    const int64_t tails = (int64_t)build_mtile_prefix(g.offsets, E, 256, mt_tail, scan_tmp, kTilesTail) * ntn;
+    build_padded_offsets(s_off, E, s_poff, scan_tmp);
+
+    // roles: per die, P8 workgroups (the launch is a multiple of 8 of them)
+    const int P8 = gridDim.x / kXcds, xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+    int nB = 0;
+    if (tails > 0) {
+        if (full == 0) {
+            nB = P8;
+        } else {
+            const int64_t wa = 100 * full, wb = MOE_TAIL_WEIGHT * tails;
+            nB = (int)(((int64_t)P8 * wb + (wa + wb) / 2) / (wa + wb));
+            nB = nB < 1 ? 1 : nB > P8 - 1 ? P8 - 1 : nB;
+        }
+    }
+    const bool is_tail = slot >= P8 - nB;
+    const int64_t total = is_tail ? tails : full;
+    ItemRange range;
+    range.first = total * xcd / kXcds + (is_tail ? slot - (P8 - nB) : slot);
+    range.end = total * (xcd + 1) / kXcds;
+    range.step = is_tail ? nB : P8 - nB;
+    if (range.first >= range.end) return;
+    if (is_tail) {
+        Loader<CB, AT, false, false> ld(g, s_off, mt_tail, s_poff, ntn, wid, lane);
+        ld.tail = true;
+        pipe_run<CB, NS, EPI, AT, false, false>(g, ld, range, reinterpret_cast<uint16_t(*)[CB::BM * BK]>(ring),
+                                                reinterpret_cast<uint16_t(*)[BK * CB::BN]>(ring + NS * CB::BM * BK),
+                                                s_bias, wid, lane);
+    } else {
+        const Loader<CA, AT, false, false> ld(g, s_off, mt_full, s_poff, ntn, wid, lane);
+        pipe_run<CA, NS, EPI, AT, false, false>(g, ld, range, reinterpret_cast<uint16_t(*)[CA::BM * BK]>(ring),
+                                                reinterpret_cast<uint16_t(*)[BK * CA::BN]>(ring + NS * CA::BM * BK),
+                                                s_bias, wid, lane);
+    }
+}
+
 template <class KernelFn>
 static int persistent_blocks(KernelFn kernel, int threads) {
     int per_cu = 0;
@@ -848,9 +935,28 @@ static bool try_pipe(const GemmArgs& g, int64_t max_rows, hipStream_t st, hipErr
     return true;
 }
 
+#ifndef MOE_TAIL_SPLIT
+#define MOE_TAIL_SPLIT 1   // the first GEMM's short expert tails on 128-row tiles (ffn_gemm_bf16_split_kernel)
+#endif
+
+// the split kernel in place of the pipelined one, under the same conditions
+template <int EPI, bool AT>
+static bool try_split(const GemmArgs& g, int64_t max_rows, hipStream_t st, hipError_t* err) {
+    static const int blocks = [] {
+        const int b = persistent_blocks(ffn_gemm_bf16_split_kernel<MOE_PIPE_NS, EPI, AT>, TilePipe::NT);
+        return b / kXcds * kXcds;   // whole dies: each die splits its workgroups into the two roles
+    }();
+    if (g.E > 1024 || blocks < 2 * kXcds || 2 * item_bound<TilePipe>(g, max_rows) < (int64_t)blocks) return false;
+    hipLaunchKernelGGL((ffn_gemm_bf16_split_kernel<MOE_PIPE_NS, EPI, AT>), dim3(blocks), dim3(TilePipe::NT), 0, st, g);
+    *err = hipGetLastError();
+    return true;
+}
+
 template <int EPI, bool AT = kATiled<EPI>>
 static hipError_t launch_epi(const GemmArgs& g, int64_t max_rows, hipStream_t st) {
     hipError_t err = hipSuccess;
+    if constexpr (MOE_TAIL_SPLIT && EPI == EPI_GELU_H)
+        if (try_split<EPI, AT>(g, max_rows, st, &err)) return err;
     if (try_pipe<TilePipe, MOE_PIPE_NS, 1024, TilePipe::NW >= 8 ? 2 : 1, EPI, AT>(g, max_rows, st, &err)) return err;
     hipLaunchKernelGGL((ffn_gemm_bf16_kernel<TileSmall, EPI, AT>), dim3(small_blocks<TileSmall, EPI, AT>()),
                        dim3(TileSmall::NT), 0, st, g);

@@ -19,24 +19,34 @@
 
 namespace moe {
 
-// mt_pre[e] = sum_{e' < e} ceil(rows(e') / BM), mt_pre[E] = total m-tiles.
+// m-tiles of an expert of `rows` rows: every BM-row block (kTilesAll); the
+// whole 256-row blocks plus a remainder above 128 rows (kTilesFull, BM =
+// 256); or one tile for a remainder of 1..128 rows (kTilesTail)
+enum { kTilesAll = 0, kTilesFull = 1, kTilesTail = 2 };
+__device__ __forceinline__ int tiles_of(int rows, int BM, int mode) {
+    if (mode == kTilesFull) return (rows >> 8) + ((rows & 255) > 128 ? 1 : 0);
+    if (mode == kTilesTail) return ((rows & 255) != 0 && (rows & 255) <= 128) ? 1 : 0;
+    return (rows + BM - 1) / BM;
+}
+
+// mt_pre[e] = sum_{e' < e} tiles_of(rows(e')), mt_pre[E] = total m-tiles.
 // Needs blockDim.x <= 1024, mt_pre of E+1 ints and tmp of 32 ints in LDS.
 __device__ __forceinline__ int build_mtile_prefix(const int32_t* __restrict__ offsets, int E, int BM,
-                                                  int* mt_pre, int* tmp) {
+                                                  int* mt_pre, int* tmp, int mode = kTilesAll) {
     const int tid = threadIdx.x;
     const int per = (E + blockDim.x - 1) / blockDim.x;
     const int lo = tid * per;
     int local = 0;
     for (int e = lo; e < lo + per && e < E; ++e) {
         const int rows = offsets[e + 1] - offsets[e];
-        local += (rows + BM - 1) / BM;
+        local += tiles_of(rows, BM, mode);
     }
     const int incl = block_inclusive_scan(local, tmp);
     int run = incl - local;
     for (int e = lo; e < lo + per && e < E; ++e) {
         mt_pre[e] = run;
         const int rows = offsets[e + 1] - offsets[e];
-        run += (rows + BM - 1) / BM;
+        run += tiles_of(rows, BM, mode);
     }
     if (tid == blockDim.x - 1) mt_pre[E] = incl;
     __syncthreads();
