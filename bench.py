@@ -51,7 +51,9 @@ STAGE_KERNELS = {
     # epilogues or layouts); GEMM1 reads x_perm row-major (moe_grouped_ffn)
     # or tiled (moe_layer_forward)
     "ffn1": (", 0, false>(moe::GemmArgs)", ", 0, true>(moe::GemmArgs)",
-             ", 0, false, false, false>(moe::GemmArgs)", ", 0, true, false, false>(moe::GemmArgs)"),
+             ", 0, false, false, false>(moe::GemmArgs)", ", 0, true, false, false>(moe::GemmArgs)",
+             # the split kernel (expert tails on 128-row tiles): <NS, EPI, AT, BKC>
+             "split_kernel<4, 0, false, false>(moe::GemmArgs)", "split_kernel<4, 0, true, false>(moe::GemmArgs)"),
     "ffn2": (", 1, true>(moe::GemmArgs)", ", 1, true, false, false>(moe::GemmArgs)"),
     "combine": ("combine_kernel",),
 }

@@ -830,7 +830,7 @@ using TileTail = TileCfg<MOE_TILE_TAIL>;
 // weight tiles in the die's L2.  Every workgroup derives nB from the same
 // offsets.  Each role runs the same pipeline as ffn_gemm_bf16_pipe_kernel
 // with its own tile shape over one LDS ring.
-template <int NS, int EPI, bool AT>
+template <int NS, int EPI, bool AT, bool BKC = false>
 __global__ __launch_bounds__(TilePipe::NT, 2) void ffn_gemm_bf16_split_kernel(GemmArgs g) {
     using CA = TilePipe;
     using CB = TileTail;
@@ -871,14 +871,14 @@ __global__ __launch_bounds__(TilePipe::NT, 2) void ffn_gemm_bf16_split_kernel(Ge
     range.step = is_tail ? nB : P8 - nB;
     if (range.first >= range.end) return;
     if (is_tail) {
-        Loader<CB, AT, false, false> ld(g, s_off, mt_tail, s_poff, ntn, wid, lane);
+        Loader<CB, AT, BKC, false> ld(g, s_off, mt_tail, s_poff, ntn, wid, lane);
         ld.tail = true;
-        pipe_run<CB, NS, EPI, AT, false, false>(g, ld, range, reinterpret_cast<uint16_t(*)[CB::BM * BK]>(ring),
+        pipe_run<CB, NS, EPI, AT, BKC, false>(g, ld, range, reinterpret_cast<uint16_t(*)[CB::BM * BK]>(ring),
                                                 reinterpret_cast<uint16_t(*)[BK * CB::BN]>(ring + NS * CB::BM * BK),
                                                 s_bias, wid, lane);
     } else {
-        const Loader<CA, AT, false, false> ld(g, s_off, mt_full, s_poff, ntn, wid, lane);
-        pipe_run<CA, NS, EPI, AT, false, false>(g, ld, range, reinterpret_cast<uint16_t(*)[CA::BM * BK]>(ring),
+        const Loader<CA, AT, BKC, false> ld(g, s_off, mt_full, s_poff, ntn, wid, lane);
+        pipe_run<CA, NS, EPI, AT, BKC, false>(g, ld, range, reinterpret_cast<uint16_t(*)[CA::BM * BK]>(ring),
                                                 reinterpret_cast<uint16_t(*)[BK * CA::BN]>(ring + NS * CA::BM * BK),
                                                 s_bias, wid, lane);
     }
@@ -940,14 +940,15 @@ static bool try_pipe(const GemmArgs& g, int64_t max_rows, hipStream_t st, hipErr
 #endif
 
 // the split kernel in place of the pipelined one, under the same conditions
-template <int EPI, bool AT>
+template <int EPI, bool AT, bool BKC = false>
 static bool try_split(const GemmArgs& g, int64_t max_rows, hipStream_t st, hipError_t* err) {
     static const int blocks = [] {
-        const int b = persistent_blocks(ffn_gemm_bf16_split_kernel<MOE_PIPE_NS, EPI, AT>, TilePipe::NT);
+        const int b = persistent_blocks(ffn_gemm_bf16_split_kernel<MOE_PIPE_NS, EPI, AT, BKC>, TilePipe::NT);
         return b / kXcds * kXcds;   // whole dies: each die splits its workgroups into the two roles
     }();
     if (g.E > 1024 || blocks < 2 * kXcds || 2 * item_bound<TilePipe>(g, max_rows) < (int64_t)blocks) return false;
-    hipLaunchKernelGGL((ffn_gemm_bf16_split_kernel<MOE_PIPE_NS, EPI, AT>), dim3(blocks), dim3(TilePipe::NT), 0, st, g);
+    hipLaunchKernelGGL((ffn_gemm_bf16_split_kernel<MOE_PIPE_NS, EPI, AT, BKC>), dim3(blocks), dim3(TilePipe::NT), 0,
+                       st, g);
     *err = hipGetLastError();
     return true;
 }
@@ -973,6 +974,11 @@ bool launch_ffn_gemm_bf16_pipe(const GemmArgs& g, int epi, bool b_kc, int64_t ma
                                hipError_t* err) {
     constexpr int WPE = TilePipe::NW >= 8 ? 2 : 1;
     if (b_kc && g.K % BK != 0) return false;   // both operands K-contiguous: no zero rows under a K tail
+    // the recompute and dh have GEMM1's shape: expert tails on 128-row tiles too
+    if constexpr (MOE_TAIL_SPLIT) {
+        if (epi == EPI_HGRAD && !b_kc && try_split<EPI_HGRAD, false>(g, max_rows, st, err)) return true;
+        if (epi == EPI_DA && b_kc && try_split<EPI_DA, false, true>(g, max_rows, st, err)) return true;
+    }
     if (epi == EPI_HGRAD && !b_kc) return try_pipe<TilePipe, MOE_PIPE_NS, 1024, WPE, EPI_HGRAD, false, false>(g, max_rows, st, err);
     if (epi == EPI_STORE_F32 && b_kc)
         return try_pipe<TilePipe, MOE_PIPE_NS, 1024, WPE, EPI_STORE_F32, false, true>(g, max_rows, st, err);
