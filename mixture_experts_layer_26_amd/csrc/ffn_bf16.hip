@@ -817,19 +817,20 @@ __global__ __launch_bounds__(C::NT, WPE) void ffn_gemm_bf16_pipe_kernel(GemmArgs
 #endif
 using TileTail = TileCfg<MOE_TILE_TAIL>;
 
-// The first grouped GEMM with the experts' short tails on 128-row tiles.
-// An expert of r rows has floor(r / 256) whole 256-row blocks; a remainder
-// above 128 rows is one more 256-row item, one of 1..128 rows a tail item
-// on a 128 x 256 tile (a 128-row tile costs about two thirds of a 256-row
-// one on whole launches).  Tails and full items run at the same time in one
+// The first grouped GEMM (and the backward's recompute and dh GEMMs of the
+// same shape) with the experts' short tails on 128-row tiles.  An expert
+// of r rows has floor(r / 256) whole 256-row blocks; a remainder above 128
+// rows is one more 256-row item, one of 1..128 rows a tail item on a
+// 128 x 256 tile (a 128-row tile costs about two thirds of a 256-row one on
+// whole launches).  Tails and full items run at the same time in one
 // launch, on workgroups of two roles: the last nB of each die's workgroups
 // take the tail items, the others the full ones, nB in proportion to each
-// role's work (tail items weighted 0.75: measured best of 0.65, 0.75 and
-// 0.9 on the 64-expert workloads); both lists
-// run expert by expert, so an expert's tail and full items share its
-// weight tiles in the die's L2.  Every workgroup derives nB from the same
-// offsets.  Each role runs the same pipeline as ffn_gemm_bf16_pipe_kernel
-// with its own tile shape over one LDS ring.
+// role's work (tail items weighted 0.75: the best of 0.65, 0.75 and 0.9 on
+// the 64-expert workloads).  Both lists run expert by expert, so an
+// expert's tail and full items share its weight tiles in the die's L2, and
+// no workgroup mixes stage sizes.  Every workgroup derives nB from the same
+// offsets.  Each role runs the pipeline of ffn_gemm_bf16_pipe_kernel with
+// its own tile shape over one LDS ring.
 template <int NS, int EPI, bool AT, bool BKC = false>
 __global__ __launch_bounds__(TilePipe::NT, 2) void ffn_gemm_bf16_split_kernel(GemmArgs g) {
     using CA = TilePipe;
