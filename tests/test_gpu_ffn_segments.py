@@ -1,10 +1,11 @@
 """The grouped expert FFN on chosen row segments (moe_grouped_ffn with given
-offsets and x_perm): expert row counts at every boundary the first GEMM's
-tile split uses (whole 256-row blocks, remainders of 1..128 rows on 128-row
-tiles, remainders above 128 on 256-row tiles) and empty experts, every row
-compared with the oracle's FFN of that row.  Also the same segments through
-the 256 x 256 tiles alone would give the same rows: each row's output depends
-on its own x row and its expert's weights only."""
+offsets and x_perm): expert row counts at every boundary the tile split uses
+(whole 256-row blocks, remainders of 1..128 rows on 128-row tiles, remainders
+above 128 on 256-row tiles) and empty experts, every row compared with the
+oracle's FFN of that row.  With a wide d_ff the first GEMM has enough items for
+the split launch (tails on 128-row tiles); with a wide d the second GEMM runs
+on the 256 x 256 pipelined tiles, and d_ff = 200 gives it an odd K-step count
+(one all-zero step per item)."""
 import numpy as np
 import pytest
 
@@ -24,7 +25,8 @@ def moe():
     return m
 
 
-@pytest.mark.parametrize("d,d_ff", [(256, 2048), (200, 1992)])   # >= 128 items: the split kernel runs
+# >= 128 items of 256 columns: the split launch (GEMM1, d_ff wide) or the pipelined one (GEMM2, d wide)
+@pytest.mark.parametrize("d,d_ff", [(256, 2048), (200, 1992), (2048, 512), (1992, 200)])
 def test_segments_at_tile_boundaries(moe, orc, d, d_ff):
     import torch
     E = len(SIZES)
