@@ -831,7 +831,17 @@ using TileTail = TileCfg<MOE_TILE_TAIL>;
 // no workgroup mixes stage sizes.  Every workgroup derives nB from the same
 // offsets.  Each role runs the pipeline of ffn_gemm_bf16_pipe_kernel with
 // its own tile shape over one LDS ring.
-template <int NS, int EPI, bool AT, bool BKC = false>
+//
+// SEQ: every workgroup runs both kinds, its full items first and its tails
+// after them, for launches with few items per workgroup (the second GEMM:
+// 2.6 at the 64-expert workload), where one more full item for some
+// workgroups decides the launch time.  Each die's full items go round robin
+// over all its workgroups, exactly as in ffn_gemm_bf16_pipe_kernel, and its
+// tails round robin from the first workgroup left with one full item fewer:
+// the busiest workgroups then run e.g. two full items and one tail instead of
+// three full items.  The tails run as a last round and re-read their weight
+// tiles (their experts' full items ran earlier).
+template <int NS, int EPI, bool AT, bool BKC = false, bool SEQ = false>
 __global__ __launch_bounds__(TilePipe::NT, 2) void ffn_gemm_bf16_split_kernel(GemmArgs g) {
     using CA = TilePipe;
     using CB = TileTail;
@@ -852,8 +862,31 @@ __global__ __launch_bounds__(TilePipe::NT, 2) void ffn_gemm_bf16_split_kernel(Ge
     const int64_t tails = (int64_t)build_mtile_prefix(g.offsets, E, 256, mt_tail, scan_tmp, kTilesTail) * ntn;
     build_padded_offsets(s_off, E, s_poff, scan_tmp);
 
-    // roles: per die, P8 workgroups (the launch is a multiple of 8 of them)
     const int P8 = gridDim.x / kXcds, xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+    if constexpr (SEQ) {
+        const int64_t f0 = full * xcd / kXcds, f1 = full * (xcd + 1) / kXcds;
+        const int64_t t0 = tails * xcd / kXcds, t1 = tails * (xcd + 1) / kXcds;
+        const int remF = (int)((f1 - f0) % P8);
+        const ItemRange rf{f0 + slot, f1, P8};
+        const ItemRange rt{t0 + (slot - remF + P8) % P8, t1, P8};
+        if (rf.first < rf.end) {
+            const Loader<CA, AT, BKC, false> ld(g, s_off, mt_full, s_poff, ntn, wid, lane);
+            pipe_run<CA, NS, EPI, AT, BKC, false>(g, ld, rf, reinterpret_cast<uint16_t(*)[CA::BM * BK]>(ring),
+                                                    reinterpret_cast<uint16_t(*)[BK * CA::BN]>(ring + NS * CA::BM * BK),
+                                                    s_bias, wid, lane);
+        }
+        if (rt.first < rt.end) {
+            // every wave is done with the ring and the bias slots of the full items
+            __syncthreads();
+            Loader<CB, AT, BKC, false> ld(g, s_off, mt_tail, s_poff, ntn, wid, lane);
+            ld.tail = true;
+            pipe_run<CB, NS, EPI, AT, BKC, false>(g, ld, rt, reinterpret_cast<uint16_t(*)[CB::BM * BK]>(ring),
+                                                    reinterpret_cast<uint16_t(*)[BK * CB::BN]>(ring + NS * CB::BM * BK),
+                                                    s_bias, wid, lane);
+        }
+        return;
+    }
+    // roles: per die, P8 workgroups (the launch is a multiple of 8 of them)
     int nB = 0;
     if (tails > 0) {
         if (full == 0) {
@@ -939,17 +972,20 @@ static bool try_pipe(const GemmArgs& g, int64_t max_rows, hipStream_t st, hipErr
 #ifndef MOE_TAIL_SPLIT
 #define MOE_TAIL_SPLIT 1   // the first GEMM's short expert tails on 128-row tiles (ffn_gemm_bf16_split_kernel)
 #endif
+#ifndef MOE_TAIL_SEQ
+#define MOE_TAIL_SEQ 1   // the second GEMM's: after each workgroup's full items (SEQ)
+#endif
 
 // the split kernel in place of the pipelined one, under the same conditions
-template <int EPI, bool AT, bool BKC = false>
+template <int EPI, bool AT, bool BKC = false, bool SEQ = false>
 static bool try_split(const GemmArgs& g, int64_t max_rows, hipStream_t st, hipError_t* err) {
     static const int blocks = [] {
-        const int b = persistent_blocks(ffn_gemm_bf16_split_kernel<MOE_PIPE_NS, EPI, AT, BKC>, TilePipe::NT);
+        const int b = persistent_blocks(ffn_gemm_bf16_split_kernel<MOE_PIPE_NS, EPI, AT, BKC, SEQ>, TilePipe::NT);
         return b / kXcds * kXcds;   // whole dies: each die splits its workgroups into the two roles
     }();
     if (g.E > 1024 || blocks < 2 * kXcds || 2 * item_bound<TilePipe>(g, max_rows) < (int64_t)blocks) return false;
-    hipLaunchKernelGGL((ffn_gemm_bf16_split_kernel<MOE_PIPE_NS, EPI, AT, BKC>), dim3(blocks), dim3(TilePipe::NT), 0,
-                       st, g);
+    hipLaunchKernelGGL((ffn_gemm_bf16_split_kernel<MOE_PIPE_NS, EPI, AT, BKC, SEQ>), dim3(blocks), dim3(TilePipe::NT),
+                       0, st, g);
     *err = hipGetLastError();
     return true;
 }
@@ -959,6 +995,8 @@ static hipError_t launch_epi(const GemmArgs& g, int64_t max_rows, hipStream_t st
     hipError_t err = hipSuccess;
     if constexpr (MOE_TAIL_SPLIT && EPI == EPI_GELU_H)
         if (try_split<EPI, AT>(g, max_rows, st, &err)) return err;
+    if constexpr (MOE_TAIL_SEQ && EPI == EPI_STORE_F32)
+        if (try_split<EPI, AT, false, true>(g, max_rows, st, &err)) return err;
     if (try_pipe<TilePipe, MOE_PIPE_NS, 1024, TilePipe::NW >= 8 ? 2 : 1, EPI, AT>(g, max_rows, st, &err)) return err;
     hipLaunchKernelGGL((ffn_gemm_bf16_kernel<TileSmall, EPI, AT>), dim3(small_blocks<TileSmall, EPI, AT>()),
                        dim3(TileSmall::NT), 0, st, g);
@@ -981,6 +1019,10 @@ bool launch_ffn_gemm_bf16_pipe(const GemmArgs& g, int epi, bool b_kc, int64_t ma
         if (epi == EPI_DA && b_kc && try_split<EPI_DA, false, true>(g, max_rows, st, err)) return true;
     }
     if (epi == EPI_HGRAD && !b_kc) return try_pipe<TilePipe, MOE_PIPE_NS, 1024, WPE, EPI_HGRAD, false, false>(g, max_rows, st, err);
+    // dx_perm has the second GEMM's shape: tails after the full items too
+    if constexpr (MOE_TAIL_SEQ)
+        if (epi == EPI_STORE_F32 && b_kc && try_split<EPI_STORE_F32, false, true, true>(g, max_rows, st, err))
+            return true;
     if (epi == EPI_STORE_F32 && b_kc)
         return try_pipe<TilePipe, MOE_PIPE_NS, 1024, WPE, EPI_STORE_F32, false, true>(g, max_rows, st, err);
     if (epi == EPI_DA && b_kc) return try_pipe<TilePipe, MOE_PIPE_NS, 1024, WPE, EPI_DA, false, true>(g, max_rows, st, err);
