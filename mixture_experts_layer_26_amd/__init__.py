@@ -137,8 +137,9 @@ def moe_stage_names() -> List[str]:
 
 
 def moe_set_stage_events(events: Sequence) -> None:
-    """events: 2 * n_stages torch.cuda.Event (or None), created with enable_timing."""
-    arr = (_P * len(events))(*[None if e is None else e.cuda_event for e in events])
+    """events: 2 * n_stages timing events (or None): torch.cuda.Event created
+    with enable_timing, or raw hipEvent_t handles as ints."""
+    arr = (_P * len(events))(*[None if e is None else e if isinstance(e, int) else e.cuda_event for e in events])
     _check(_lib.moe_set_stage_events(arr, len(events)))
 
 
