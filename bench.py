@@ -52,12 +52,10 @@ STAGE_KERNELS = {
     # or tiled (moe_layer_forward)
     "ffn1": (", 0, false>(moe::GemmArgs)", ", 0, true>(moe::GemmArgs)",
              ", 0, false, false, false>(moe::GemmArgs)", ", 0, true, false, false>(moe::GemmArgs)",
-             # the split kernel (expert tails on 128-row tiles): <NS, EPI, AT, BKC, SEQ>
-             "split_kernel<4, 0, false, false, false>(moe::GemmArgs)",
-             "split_kernel<4, 0, true, false, false>(moe::GemmArgs)"),
+             # the split kernel (expert tails on 128-row tiles): <NS, EPI, AT, BKC>
+             "split_kernel<4, 0, false, false>(moe::GemmArgs)", "split_kernel<4, 0, true, false>(moe::GemmArgs)"),
     "ffn2": (", 1, true>(moe::GemmArgs)", ", 1, true, false, false>(moe::GemmArgs)",
-             # the split kernel in SEQ mode (each workgroup's full items, then its tails)
-             "split_kernel<4, 1, true, false, true>(moe::GemmArgs)"),
+             "split_kernel<4, 1, true, false>(moe::GemmArgs)"),
     "combine": ("combine_kernel",),
 }
 

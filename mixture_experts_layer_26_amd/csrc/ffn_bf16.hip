@@ -832,16 +832,22 @@ using TileTail = TileCfg<MOE_TILE_TAIL>;
 // offsets.  Each role runs the pipeline of ffn_gemm_bf16_pipe_kernel with
 // its own tile shape over one LDS ring.
 //
-// SEQ: every workgroup runs both kinds, its full items first and its tails
-// after them, for launches with few items per workgroup (the second GEMM:
-// 2.6 at the 64-expert workload), where one more full item for some
-// workgroups decides the launch time.  Each die's full items go round robin
-// over all its workgroups, exactly as in ffn_gemm_bf16_pipe_kernel, and its
-// tails round robin from the first workgroup left with one full item fewer:
-// the busiest workgroups then run e.g. two full items and one tail instead of
-// three full items.  The tails run as a last round and re-read their weight
-// tiles (their experts' full items ran earlier).
-template <int NS, int EPI, bool AT, bool BKC = false, bool SEQ = false>
+// Where a die has at most MOE_SEQ_MAX_FULL full items per workgroup (the
+// second GEMM at the 64-expert workload: 2, at 128 experts: 4; the first at
+// 16 experts: 2), one more full item for some workgroups decides the launch
+// time and the roles cannot help (measured: sequenced wins up to 4, roles at
+// 8).  Such a die runs sequenced instead: every workgroup takes both
+// kinds, its full items first and its tails after them.  The die's full items
+// go round robin over all its workgroups, exactly as in
+// ffn_gemm_bf16_pipe_kernel, and its tails round robin from the first
+// workgroup left with one full item fewer: the busiest workgroups then run
+// e.g. two full items and one tail instead of three full items.  The tails run
+// as a last round and re-read their weight tiles (their experts' full items
+// ran earlier).  Every workgroup of a die takes the same decision.
+#ifndef MOE_SEQ_MAX_FULL
+#define MOE_SEQ_MAX_FULL 4
+#endif
+template <int NS, int EPI, bool AT, bool BKC = false>
 __global__ __launch_bounds__(TilePipe::NT, 2) void ffn_gemm_bf16_split_kernel(GemmArgs g) {
     using CA = TilePipe;
     using CB = TileTail;
@@ -863,8 +869,8 @@ __global__ __launch_bounds__(TilePipe::NT, 2) void ffn_gemm_bf16_split_kernel(Ge
     build_padded_offsets(s_off, E, s_poff, scan_tmp);
 
     const int P8 = gridDim.x / kXcds, xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
-    if constexpr (SEQ) {
-        const int64_t f0 = full * xcd / kXcds, f1 = full * (xcd + 1) / kXcds;
+    const int64_t f0 = full * xcd / kXcds, f1 = full * (xcd + 1) / kXcds;
+    if (tails > 0 && f1 - f0 <= (int64_t)MOE_SEQ_MAX_FULL * P8) {
         const int64_t t0 = tails * xcd / kXcds, t1 = tails * (xcd + 1) / kXcds;
         const int remF = (int)((f1 - f0) % P8);
         const ItemRange rf{f0 + slot, f1, P8};
@@ -972,19 +978,19 @@ static bool try_pipe(const GemmArgs& g, int64_t max_rows, hipStream_t st, hipErr
 #ifndef MOE_TAIL_SPLIT
 #define MOE_TAIL_SPLIT 1   // the first GEMM's short expert tails on 128-row tiles (ffn_gemm_bf16_split_kernel)
 #endif
-#ifndef MOE_TAIL_SEQ
-#define MOE_TAIL_SEQ 1   // the second GEMM's: after each workgroup's full items (SEQ)
+#ifndef MOE_TAIL_SPLIT2
+#define MOE_TAIL_SPLIT2 1   // the second GEMM's and dx_perm's too (roles or sequenced, per die)
 #endif
 
 // the split kernel in place of the pipelined one, under the same conditions
-template <int EPI, bool AT, bool BKC = false, bool SEQ = false>
+template <int EPI, bool AT, bool BKC = false>
 static bool try_split(const GemmArgs& g, int64_t max_rows, hipStream_t st, hipError_t* err) {
     static const int blocks = [] {
-        const int b = persistent_blocks(ffn_gemm_bf16_split_kernel<MOE_PIPE_NS, EPI, AT, BKC, SEQ>, TilePipe::NT);
+        const int b = persistent_blocks(ffn_gemm_bf16_split_kernel<MOE_PIPE_NS, EPI, AT, BKC>, TilePipe::NT);
         return b / kXcds * kXcds;   // whole dies: each die splits its workgroups into the two roles
     }();
     if (g.E > 1024 || blocks < 2 * kXcds || 2 * item_bound<TilePipe>(g, max_rows) < (int64_t)blocks) return false;
-    hipLaunchKernelGGL((ffn_gemm_bf16_split_kernel<MOE_PIPE_NS, EPI, AT, BKC, SEQ>), dim3(blocks), dim3(TilePipe::NT),
+    hipLaunchKernelGGL((ffn_gemm_bf16_split_kernel<MOE_PIPE_NS, EPI, AT, BKC>), dim3(blocks), dim3(TilePipe::NT),
                        0, st, g);
     *err = hipGetLastError();
     return true;
@@ -995,8 +1001,8 @@ static hipError_t launch_epi(const GemmArgs& g, int64_t max_rows, hipStream_t st
     hipError_t err = hipSuccess;
     if constexpr (MOE_TAIL_SPLIT && EPI == EPI_GELU_H)
         if (try_split<EPI, AT>(g, max_rows, st, &err)) return err;
-    if constexpr (MOE_TAIL_SEQ && EPI == EPI_STORE_F32)
-        if (try_split<EPI, AT, false, true>(g, max_rows, st, &err)) return err;
+    if constexpr (MOE_TAIL_SPLIT2 && EPI == EPI_STORE_F32)
+        if (try_split<EPI, AT>(g, max_rows, st, &err)) return err;
     if (try_pipe<TilePipe, MOE_PIPE_NS, 1024, TilePipe::NW >= 8 ? 2 : 1, EPI, AT>(g, max_rows, st, &err)) return err;
     hipLaunchKernelGGL((ffn_gemm_bf16_kernel<TileSmall, EPI, AT>), dim3(small_blocks<TileSmall, EPI, AT>()),
                        dim3(TileSmall::NT), 0, st, g);
@@ -1019,10 +1025,9 @@ bool launch_ffn_gemm_bf16_pipe(const GemmArgs& g, int epi, bool b_kc, int64_t ma
         if (epi == EPI_DA && b_kc && try_split<EPI_DA, false, true>(g, max_rows, st, err)) return true;
     }
     if (epi == EPI_HGRAD && !b_kc) return try_pipe<TilePipe, MOE_PIPE_NS, 1024, WPE, EPI_HGRAD, false, false>(g, max_rows, st, err);
-    // dx_perm has the second GEMM's shape: tails after the full items too
-    if constexpr (MOE_TAIL_SEQ)
-        if (epi == EPI_STORE_F32 && b_kc && try_split<EPI_STORE_F32, false, true, true>(g, max_rows, st, err))
-            return true;
+    // dx_perm has the second GEMM's shape
+    if constexpr (MOE_TAIL_SPLIT2)
+        if (epi == EPI_STORE_F32 && b_kc && try_split<EPI_STORE_F32, false, true>(g, max_rows, st, err)) return true;
     if (epi == EPI_STORE_F32 && b_kc)
         return try_pipe<TilePipe, MOE_PIPE_NS, 1024, WPE, EPI_STORE_F32, false, true>(g, max_rows, st, err);
     if (epi == EPI_DA && b_kc) return try_pipe<TilePipe, MOE_PIPE_NS, 1024, WPE, EPI_DA, false, true>(g, max_rows, st, err);
