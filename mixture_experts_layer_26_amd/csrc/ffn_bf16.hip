@@ -47,6 +47,10 @@
 //     register set while its MFMAs run, and the ring continues across items.
 //   * small problems: 128 x 128 tiles, four waves on v_mfma_f32_16x16x32_bf16,
 //     one barrier per step (read, then multiply).
+// Expert tails (an expert's last 1..128 rows) run on 128 x 256 tiles of the
+// same eight waves in ffn_gemm_bf16_split_kernel: on workgroups of their own
+// beside the full items, or after each workgroup's full items where a die has
+// few of them (see there).
 #include "ffn_sched.h"
 #include "lds_dma.h"
 #include "moe_kernels.h"
