@@ -847,7 +847,9 @@ using TileTail = TileCfg<MOE_TILE_TAIL>;
 // workgroup left with one full item fewer: the busiest workgroups then run
 // e.g. two full items and one tail instead of three full items.  The tails run
 // as a last round and re-read their weight tiles (their experts' full items
-// ran earlier).  Every workgroup of a die takes the same decision.
+// ran earlier).  Every workgroup of a die takes the same decision; dies
+// decide apart (their full-item counts may differ by one), and either way a
+// die covers exactly its own share of both lists.
 #ifndef MOE_SEQ_MAX_FULL
 #define MOE_SEQ_MAX_FULL 4
 #endif
