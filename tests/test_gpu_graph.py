@@ -19,7 +19,8 @@ def moe():
     return m
 
 
-@pytest.mark.parametrize("name", ["medium_bf16", "ragged_fp32", "soft_k64_e64"])
+# bf16_e16: both GEMMs on the 256 x 256 tiles with the experts' tails on 128-row tiles
+@pytest.mark.parametrize("name", ["medium_bf16", "ragged_fp32", "soft_k64_e64", "bf16_e16"])
 def test_forward_graph_replays_match_eager(moe, name):
     import torch
     cfg = get(name)
